@@ -1,0 +1,31 @@
+"""FP64 CPU oracle for streaming (online-softmax) attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+load anything from this package: only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code,
+constants or helpers with the HIP library under
+``online_softmax_streaming_amd/``, and it imports nothing from there.
+
+Sources (three web pages on one subject):
+  * "Intermediate and advanced kernel workshops" (the workshops page):
+    section "Scope and contracts" -- the streaming_attention contract.
+  * "Compare reasoning after your own attempt" (the answer-key page):
+    the A1 / A3 rows of its table, "Worked answers worth memorizing by
+    derivation" (A1 merge, A3 six/seven example) and the closing note that the
+    attention oracle materialises FP64 scores.
+  * "Kernel Notes & Checklist": section 4, "The gotchas ledger" (-inf padding
+    before a max, 0 before a sum, ghost rows pinned so they cannot give NaN).
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against values
+the pages print, closed forms, invariants and 50-digit brute force.
+"""
+
+from .attention import (  # noqa: F401
+    EMPTY_STATE,
+    attention,
+    attention_rows,
+    merge_state_of,
+    online_merge,
+    streaming_model,
+    visible_mask,
+)

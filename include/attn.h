@@ -1,0 +1,157 @@
+/*
+ * attn.h -- C ABI of the streaming (online-softmax) attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what the calls compute (three web pages on one subject):
+ *   [W]  "Intermediate and advanced kernel workshops", section "Scope and
+ *        contracts", rows streaming_attention and split_softmax, and the
+ *        paragraph after the table (single-head, forward only, P cast to the
+ *        input precision before the P.V product).
+ *   [AK] "Compare reasoning after your own attempt" (the answer key): table
+ *        rows A1, A2, A3 and "Worked answers worth memorizing by derivation".
+ *   [KN] "Kernel Notes & Checklist", section 4, "The gotchas ledger".
+ *
+ * Conventions shared by every call:
+ *   - Plain pointers and sizes only.  Device pointers point to memory of the
+ *     current HIP device; the caller owns every buffer and keeps it alive
+ *     until the work queued on `stream` has finished.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is queued asynchronously; no call synchronises the host.
+ *   - Argument errors are found on the host before anything is queued and
+ *     returned synchronously; nothing is written in that case.  Input
+ *     *values* are never scanned: non-finite inputs are outside the contract
+ *     ([W], "Scope and contracts": wrappers validate metadata only).
+ *   - Status codes: ATTN_OK, ATTN_E_INVALID (bad argument), ATTN_E_UNSUPPORTED
+ *     (valid but not built: head size), ATTN_E_HIP (a HIP runtime call or
+ *     kernel launch failed; the HIP error text is in attn_last_error()).
+ */
+#ifndef ONLINE_SOFTMAX_STREAMING_ATTN_H
+#define ONLINE_SOFTMAX_STREAMING_ATTN_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define ATTN_API __attribute__((visibility("default")))
+#else
+#define ATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of Q, K, V and out (all four share one type). */
+#define ATTN_F32 0  /* IEEE binary32 */
+#define ATTN_F16 1  /* IEEE binary16 */
+#define ATTN_BF16 2 /* bfloat16 */
+
+#define ATTN_OK 0
+#define ATTN_E_INVALID 1
+#define ATTN_E_UNSUPPORTED 2
+#define ATTN_E_HIP 3
+
+/*
+ * attn_fwd -- scaled-dot-product attention forward, streaming over key tiles.
+ *
+ * Computes, for every batch b < B, head h < H and query row i < Nq,
+ *
+ *     out[b,h,i,:] = sum_{j visible} softmax_j(scale * Q[b,h,i,:] . K[b,h,j,:]) V[b,h,j,:]
+ *
+ * carrying the running state (max m, sum l, unnormalised output a) across
+ * key tiles and rescaling both l and a by exp(m_old - m_new) when the max
+ * rises ([AK] row A3); the full score matrix is never formed.  Masked and
+ * padded scores are -inf before the max and contribute 0 to the sums; rows
+ * with nothing visible yet are pinned so they cannot produce NaN ([KN]).
+ *
+ * Visibility: every j < Nk when causal == 0.  When causal == 1, key j is
+ * visible to query i iff j <= i + (Nk - Nq): the diagonal is included ([W],
+ * streaming_attention row) and, for Nq != Nk, keys are aligned to the end
+ * of the query block.  A row with no visible key gets out = +0.
+ *
+ * Layout: Q and out are contiguous [B, H, Nq, D]; K and V are contiguous
+ * [B, H, Nk, D]; row-major, D fastest.  All four use `dtype`; out is
+ * written with one round-to-nearest-even cast from the FP32 result.
+ * Arithmetic: FP32 accumulation throughout; for F16/BF16 the products
+ * Q.K^T and P.V run on bf16/f16 matrix cores, with P rounded to the input
+ * type before P.V ([W], paragraph after the contracts table).
+ *
+ * Arguments:
+ *   Q, K, V, out  device pointers, 16-byte aligned; out must not overlap
+ *                 Q, K or V.  K and V may be NULL when Nk == 0.
+ *   B, H, Nq, Nk  >= 0.  B, H or Nq == 0 is a no-op returning ATTN_OK.
+ *                 Nk == 0 writes out = 0.  Per head, Nq*D and Nk*D must be
+ *                 < 2^31, and B*H < 2^31; element offsets across heads are
+ *                 64-bit, so whole tensors may exceed 2^31 elements.
+ *   D             head size: 16, 32, 64 or 128 (else ATTN_E_UNSUPPORTED).
+ *   causal        0 or 1.
+ *   scale         logit scale, finite and > 0 (the pages use 1/sqrt(D)).
+ *   dtype         ATTN_F32, ATTN_F16 or ATTN_BF16.
+ *   stream        hipStream_t the work is queued on.
+ *
+ * Memory: the prefill path (Nq > 8) allocates nothing.  The split-key
+ * decode path (Nq <= 8) needs a scratch array of partial states, taken
+ * stream-ordered with hipMallocAsync / hipFreeAsync on `stream`.
+ */
+ATTN_API int attn_fwd(const void* Q, const void* K, const void* V, void* out,
+             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+             int causal, float scale, int dtype, void* stream);
+
+/*
+ * attn_fwd_stats -- attn_fwd that also returns each row's merge state.
+ *
+ * Same arguments and behaviour as attn_fwd, plus two optional FP32 device
+ * arrays of B*H*Nq elements, row-major [B, H, Nq]:
+ *   m_out[row]  the row's maximum scaled logit, natural-log units;
+ *   l_out[row]  sum over visible keys of exp(scale * q.k - m_out).
+ * Together they are the row's A1 state ([AK] row A1): the sum of
+ * exp(scale * q.k) over visible keys equals l * exp(m).  A row with no
+ * visible key has (m, l) = (-inf, 0).  Either pointer may be NULL.
+ */
+ATTN_API int attn_fwd_stats(const void* Q, const void* K, const void* V, void* out,
+                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                   int causal, float scale, int dtype,
+                   float* m_out, float* l_out, void* stream);
+
+/*
+ * online_merge -- merge two A1 summaries ([AK] row A1 and its worked answer).
+ *
+ * A state (m, l) stands for sum_j exp(x_j) = l * exp(m); (-inf, 0) is the
+ * empty state.  The result re-expresses both relative to the common maximum:
+ *     m = max(m1, m2),  l = l1 * exp(m1 - m) + l2 * exp(m2 - m),
+ * and merging two empty states gives the empty state, never NaN.
+ * Example: (2, 2) merged with (4, 1) is (4, 1 + 2 exp(-2)).
+ *
+ * Host call in double precision; m and l are host pointers, both non-NULL
+ * (else ATTN_E_INVALID).  l1 and l2 must be >= 0 and the m's must not be
+ * NaN or +inf (else ATTN_E_INVALID).  Touches no device.
+ */
+ATTN_API int online_merge(double m1, double l1, double m2, double l2,
+                 double* m, double* l);
+
+/*
+ * online_merge_batch -- the same merge, elementwise on device arrays.
+ *
+ * m1, l1, m2, l2, m, l: FP32 device arrays of n elements (natural-log
+ * units, as written by attn_fwd_stats).  Outputs may alias inputs
+ * elementwise.  The split-key decode path folds its partial states with
+ * the same merge, in base-2 units inside its kernels ([AK] row A2: partial
+ * statistics, then a rescaled merge, on one stream).  Queued on `stream`;
+ * n == 0 is a no-op; n < 0 or a NULL or misaligned array is
+ * ATTN_E_INVALID.
+ */
+ATTN_API int online_merge_batch(const float* m1, const float* l1,
+                       const float* m2, const float* l2,
+                       float* m, float* l, int64_t n, void* stream);
+
+/* Static text for a status code; never NULL. */
+ATTN_API const char* attn_strerror(int code);
+
+/* Detail of the last ATTN_E_INVALID / ATTN_E_HIP on the calling thread
+ * (empty string if none); valid until the next call on that thread. */
+ATTN_API const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ONLINE_SOFTMAX_STREAMING_ATTN_H */

@@ -1,0 +1,24 @@
+"""Streaming (online-softmax) attention forward for AMD MI355X (gfx950).
+
+The computation lives in the HIP library libattn.so (C ABI in
+include/attn.h); this package is its Python binding plus the seeded
+workload definitions used by the tests and the benchmark.
+"""
+
+from .attn import (  # noqa: F401
+    ATTN_BF16,
+    ATTN_E_HIP,
+    ATTN_E_INVALID,
+    ATTN_E_UNSUPPORTED,
+    ATTN_F16,
+    ATTN_F32,
+    ATTN_OK,
+    AttnError,
+    attn_fwd,
+    attn_fwd_raw,
+    attn_fwd_stats,
+    attn_strerror,
+    default_scale,
+    online_merge,
+    online_merge_batch,
+)

@@ -1,0 +1,54 @@
+"""ctypes loader for the in-tree HIP library libattn.so.
+
+There is no fallback: if the library has not been built, or cannot be
+loaded, every call raises.  Build it with ``__graft_entry__.build()`` or
+``python online_softmax_streaming_amd/build.py``.
+"""
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+_lock = threading.Lock()
+_lib = None
+
+_c_i64 = ctypes.c_int64
+_c_ptr = ctypes.c_void_p
+_c_fptr = ctypes.POINTER(ctypes.c_float)
+
+# Exported symbols and their C signatures, as declared in include/attn.h.
+SIGNATURES = {
+    "attn_fwd": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_i64,
+                                _c_i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, _c_ptr]),
+    "attn_fwd_stats": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64,
+                                      _c_i64, _c_i64, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                      _c_ptr, _c_ptr, _c_ptr]),
+    "online_merge": (ctypes.c_int, [ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                    ctypes.c_double, ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_double)]),
+    "online_merge_batch": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64,
+                                          _c_ptr]),
+    "attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "attn_last_error": (ctypes.c_char_p, []),
+}
+
+
+def lib():
+    """The loaded library (loaded once per process)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"HIP library {LIB_PATH} is not built; run __graft_entry__.build()")
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(handle, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = handle
+    return _lib

@@ -1,0 +1,161 @@
+"""Python binding of the C ABI in include/attn.h (argument marshalling only).
+
+Tensors are PyTorch device tensors: torch supplies the memory and the
+stream, and every step of the computation runs in the HIP kernels of
+libattn.so.  Nothing here computes attention; there is no CPU path.
+"""
+
+import ctypes
+import math
+
+import torch
+
+from ._lib import lib
+
+ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
+ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_HIP = 0, 1, 2, 3
+
+_DTYPES = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+
+#: Query rows per head at or below which attn_fwd takes the split-key decode path.
+DECODE_MAX_NQ = 8
+
+
+class AttnError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, code, where):
+        self.code = code
+        detail = lib().attn_last_error().decode()
+        super().__init__(f"{where}: {attn_strerror(code)} ({code})" + (f": {detail}" if detail else ""))
+
+
+def attn_strerror(code):
+    """Text for a status code."""
+    return lib().attn_strerror(int(code)).decode()
+
+
+def _check(rc, where):
+    if rc != ATTN_OK:
+        raise AttnError(rc, where)
+
+
+def default_scale(d):
+    """1/sqrt(D) rounded to FP32, the scale the pages use."""
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+
+
+def _stream_handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _validate(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor (got {t.device}); there is no CPU path")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, N, D], got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype not in _DTYPES:
+            raise ValueError(f"{name} has unsupported dtype {t.dtype}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share one dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on one device")
+    if k.shape != v.shape:
+        raise ValueError(f"k and v shapes differ: {tuple(k.shape)} vs {tuple(v.shape)}")
+    b, h, _, d = q.shape
+    if (k.shape[0], k.shape[1], k.shape[3]) != (b, h, d):
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree on B, H or D")
+
+
+def attn_fwd_stats(q, k, v, causal=False, scale=None, out=None, m_out=None, l_out=None,
+                   stream=None, want_stats=True):
+    """Streaming attention forward; returns (out, m, l).
+
+    q: [B, H, Nq, D]; k, v: [B, H, Nk, D]; one dtype (float32, float16 or
+    bfloat16), contiguous, on one GPU.  ``out`` (same shape/dtype as q) and
+    the float32 [B, H, Nq] arrays ``m_out`` / ``l_out`` are allocated when not
+    given.  ``scale`` defaults to FP32(1/sqrt(D)).  The work is queued on
+    ``stream`` (default: torch's current stream of q's device).
+    """
+    _validate(q, k, v)
+    b, h, nq, d = q.shape
+    nk = k.shape[2]
+    if scale is None:
+        scale = default_scale(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor like q")
+    if want_stats:
+        for name, t in (("m_out", m_out), ("l_out", l_out)):
+            if t is not None and (t.dtype != torch.float32 or t.device != q.device
+                                  or t.shape != (b, h, nq) or not t.is_contiguous()):
+                raise ValueError(f"{name} must be a contiguous float32 [B, H, Nq] GPU tensor")
+        if m_out is None:
+            m_out = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
+        if l_out is None:
+            l_out = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        sh = _stream_handle(stream, q.device)
+        args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                b, h, nq, nk, d, int(bool(causal)), float(scale), _DTYPES[q.dtype])
+        if want_stats:
+            rc = lib().attn_fwd_stats(*args, ctypes.c_void_p(m_out.data_ptr()),
+                                      ctypes.c_void_p(l_out.data_ptr()), sh)
+            _check(rc, "attn_fwd_stats")
+        else:
+            _check(lib().attn_fwd(*args, sh), "attn_fwd")
+    return out, m_out, l_out
+
+
+def attn_fwd(q, k, v, causal=False, scale=None, out=None, stream=None):
+    """Streaming attention forward; returns ``out`` [B, H, Nq, D]."""
+    return attn_fwd_stats(q, k, v, causal=causal, scale=scale, out=out, stream=stream,
+                          want_stats=False)[0]
+
+
+def attn_fwd_raw(q_ptr, k_ptr, v_ptr, out_ptr, b, h, nq, nk, d, causal, scale, dtype,
+                 stream_handle=0):
+    """Direct C call with raw device pointers; returns the status code."""
+    return lib().attn_fwd(ctypes.c_void_p(q_ptr), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
+                          ctypes.c_void_p(out_ptr), b, h, nq, nk, d, int(causal), float(scale),
+                          int(dtype), ctypes.c_void_p(stream_handle))
+
+
+def online_merge(m1, l1, m2, l2):
+    """Host A1 merge in double precision; returns (m, l)."""
+    m = ctypes.c_double()
+    l = ctypes.c_double()
+    _check(lib().online_merge(float(m1), float(l1), float(m2), float(l2), ctypes.byref(m),
+                              ctypes.byref(l)), "online_merge")
+    return m.value, l.value
+
+
+def online_merge_batch(m1, l1, m2, l2, m=None, l=None, stream=None):
+    """Elementwise A1 merge of float32 GPU tensors of one shape; returns (m, l)."""
+    ts = (m1, l1, m2, l2)
+    for t in ts:
+        if (not isinstance(t, torch.Tensor) or t.device.type != "cuda"
+                or t.dtype != torch.float32 or not t.is_contiguous() or t.shape != m1.shape
+                or t.device != m1.device):
+            raise ValueError("online_merge_batch takes contiguous float32 GPU tensors of one shape")
+    m = torch.empty_like(m1) if m is None else m
+    l = torch.empty_like(m1) if l is None else l
+    for t in (m, l):
+        if t.shape != m1.shape or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("outputs must be contiguous float32 tensors like the inputs")
+    with torch.cuda.device(m1.device):
+        sh = _stream_handle(stream, m1.device)
+        rc = lib().online_merge_batch(*(ctypes.c_void_p(t.data_ptr()) for t in (*ts, m, l)),
+                                      m1.numel(), sh)
+    _check(rc, "online_merge_batch")
+    return m, l

@@ -1,0 +1,198 @@
+// C ABI of the attention library: argument checks, path selection and the
+// host form of the A1 merge.  The contract of each call is documented in
+// include/attn.h; the checks below are the "validate metadata, never scan
+// values" rule of the workshops page ("Scope and contracts").
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/attn.h"
+#include "attn_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ATTN_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+constexpr int64_t kI32Max = 2147483647;
+
+// Keep freed stream-ordered scratch in the device's default pool instead of
+// returning it to the driver at every synchronisation.
+void keep_pool_memory() {
+  static std::mutex mu;
+  static bool done[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done[dev]) return;
+  hipMemPool_t pool;
+  if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+    uint64_t threshold = UINT64_MAX;
+    (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+  }
+  done[dev] = true;
+}
+
+int run_attention(const void* Q, const void* K, const void* V, void* out, int64_t B, int64_t H,
+                  int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, int dtype,
+                  float* m_out, float* l_out, void* stream) {
+  g_last_error[0] = '\0';
+  if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_E_INVALID, "dtype %d is not ATTN_F32, ATTN_F16 or ATTN_BF16", dtype);
+  if (causal != 0 && causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1, got %d", causal);
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+    return fail(ATTN_E_INVALID, "negative size (B=%lld H=%lld Nq=%lld Nk=%lld)", (long long)B,
+                (long long)H, (long long)Nq, (long long)Nk);
+  if (D <= 0) return fail(ATTN_E_INVALID, "D must be positive, got %lld", (long long)D);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(ATTN_E_INVALID, "scale must be finite and > 0, got %g", (double)scale);
+  if (D != 16 && D != 32 && D != 64 && D != 128)
+    return fail(ATTN_E_UNSUPPORTED, "head size D=%lld not built (16, 32, 64, 128)", (long long)D);
+  if (B > kI32Max || H > kI32Max || Nq > kI32Max || Nk > kI32Max || B * H > kI32Max ||
+      Nq * D > kI32Max || Nk * D > kI32Max || B * H * Nq > kI32Max)
+    return fail(ATTN_E_INVALID,
+                "sizes exceed the 32-bit per-head limits (B*H, Nq*D, Nk*D, B*H*Nq < 2^31)");
+  if (B == 0 || H == 0 || Nq == 0) return ATTN_OK;
+
+  const int64_t elem = dtype == ATTN_F32 ? 4 : 2;
+  if (!Q || !out) return fail(ATTN_E_INVALID, "Q and out must be non-NULL");
+  if (Nk > 0 && (!K || !V)) return fail(ATTN_E_INVALID, "K and V must be non-NULL when Nk > 0");
+  if (!aligned(Q, 16) || !aligned(out, 16) || (Nk > 0 && (!aligned(K, 16) || !aligned(V, 16))))
+    return fail(ATTN_E_INVALID, "Q, K, V and out must be 16-byte aligned");
+  if ((m_out && !aligned(m_out, 4)) || (l_out && !aligned(l_out, 4)))
+    return fail(ATTN_E_INVALID, "m_out and l_out must be 4-byte aligned");
+  const int64_t qbytes = B * H * Nq * D * elem;
+  const int64_t kbytes = B * H * Nk * D * elem;
+  const int64_t sbytes = B * H * Nq * 4;
+  if (overlaps(out, qbytes, Q, qbytes) || overlaps(out, qbytes, K, kbytes) ||
+      overlaps(out, qbytes, V, kbytes))
+    return fail(ATTN_E_INVALID, "out overlaps Q, K or V");
+  if (overlaps(m_out, sbytes, out, qbytes) || overlaps(l_out, sbytes, out, qbytes) ||
+      overlaps(m_out, sbytes, l_out, sbytes))
+    return fail(ATTN_E_INVALID, "m_out / l_out overlap out or each other");
+
+  attn::Problem p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = out;
+  p.m_out = m_out;
+  p.l_out = l_out;
+  p.B = B;
+  p.H = H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.D = D;
+  p.causal = causal != 0;
+  p.scale = scale;
+  p.dtype = static_cast<attn::DType>(dtype);
+  p.stream = static_cast<hipStream_t>(stream);
+
+  hipError_t e;
+  if (Nk == 0) {
+    e = attn::launch_fill_empty(p);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "fill kernel launch");
+  }
+  if (Nq <= attn::kDecodeMaxNq) {
+    const attn::DecodePlan plan = attn::plan_decode(p);
+    keep_pool_memory();
+    void* scratch = nullptr;
+    e = hipMallocAsync(&scratch, plan.scratch_bytes, p.stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of decode scratch");
+    e = attn::launch_decode(p, plan, static_cast<float*>(scratch));
+    const hipError_t ef = hipFreeAsync(scratch, p.stream);
+    if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of decode scratch");
+    return ATTN_OK;
+  }
+  e = dtype == ATTN_F32 ? attn::launch_prefill_f32(p) : attn::launch_prefill_mfma(p);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "prefill kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* Q, const void* K, const void* V, void* out, int64_t B, int64_t H,
+             int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, int dtype, void* stream) {
+  return run_attention(Q, K, V, out, B, H, Nq, Nk, D, causal, scale, dtype, nullptr, nullptr,
+                       stream);
+}
+
+int attn_fwd_stats(const void* Q, const void* K, const void* V, void* out, int64_t B, int64_t H,
+                   int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, int dtype,
+                   float* m_out, float* l_out, void* stream) {
+  return run_attention(Q, K, V, out, B, H, Nq, Nk, D, causal, scale, dtype, m_out, l_out, stream);
+}
+
+int online_merge(double m1, double l1, double m2, double l2, double* m, double* l) {
+  g_last_error[0] = '\0';
+  if (!m || !l) return fail(ATTN_E_INVALID, "online_merge: m and l must be non-NULL");
+  if (isnan(m1) || isnan(m2) || m1 == INFINITY || m2 == INFINITY)
+    return fail(ATTN_E_INVALID, "online_merge: m must be finite or -inf");
+  if (!(l1 >= 0.0) || !(l2 >= 0.0) || isinf(l1) || isinf(l2))
+    return fail(ATTN_E_INVALID, "online_merge: l must be finite and >= 0");
+  const double mm = m1 > m2 ? m1 : m2;
+  if (mm == -INFINITY) {  // empty with empty: the empty state, not NaN
+    *m = -INFINITY;
+    *l = 0.0;
+    return ATTN_OK;
+  }
+  *m = mm;
+  *l = l1 * exp(m1 - mm) + l2 * exp(m2 - mm);
+  return ATTN_OK;
+}
+
+int online_merge_batch(const float* m1, const float* l1, const float* m2, const float* l2,
+                       float* m, float* l, int64_t n, void* stream) {
+  g_last_error[0] = '\0';
+  if (n < 0) return fail(ATTN_E_INVALID, "online_merge_batch: n < 0");
+  if (n == 0) return ATTN_OK;
+  if (!m1 || !l1 || !m2 || !l2 || !m || !l)
+    return fail(ATTN_E_INVALID, "online_merge_batch: NULL array");
+  const void* ptrs[6] = {m1, l1, m2, l2, m, l};
+  for (const void* q : ptrs)
+    if (!aligned(q, 4)) return fail(ATTN_E_INVALID, "online_merge_batch: misaligned array");
+  const hipError_t e =
+      attn::launch_merge_batch(m1, l1, m2, l2, m, l, n, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "merge kernel launch");
+}
+
+const char* attn_strerror(int code) {
+  switch (code) {
+    case ATTN_OK: return "success";
+    case ATTN_E_INVALID: return "invalid argument";
+    case ATTN_E_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_E_HIP: return "HIP runtime error";
+    default: return "unknown status code";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

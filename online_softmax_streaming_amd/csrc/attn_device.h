@@ -1,0 +1,55 @@
+// Device-side helpers shared by the attention kernels (gfx950 only).
+//
+// The running-state arithmetic follows the answer-key page ("Compare
+// reasoning after your own attempt"), rows A1 and A3: a state (m, l) stands
+// for sum exp(x) = l * e^m; merging or extending a state re-expresses both
+// parts relative to the larger maximum, and the unnormalised output a is
+// rescaled by the same factor as l.  Inside the kernels every logit is kept
+// in base-2 units (x * log2 e), so each exponential is one v_exp_f32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kNegInf = -__builtin_inff();
+
+// 2^x with the hardware transcendental (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reference point for rescaling: the running max, or 0 while nothing has
+// been seen.  A row whose max is still -inf would otherwise compute
+// (-inf) - (-inf) = NaN ("Kernel Notes & Checklist", gotchas ledger: ghost
+// rows must be pinned).
+__device__ __forceinline__ float pinned_ref(float m) { return m == kNegInf ? 0.f : m; }
+
+// One A1 merge in base-2 units: returns the weights that carry each side to
+// the common maximum, and the new maximum.  Both weights are 0 for an empty
+// side, so merging two empty states gives the empty state.
+struct MergeWeights {
+  float m, w1, w2;
+};
+__device__ __forceinline__ MergeWeights merge_weights_log2(float m1, float m2) {
+  MergeWeights r;
+  r.m = fmaxf(m1, m2);
+  const float ref = pinned_ref(r.m);
+  r.w1 = exp2_hw(m1 - ref);
+  r.w2 = exp2_hw(m2 - ref);
+  return r;
+}
+
+// Element conversions.  Output casts are round-to-nearest-even.
+template <typename T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x) { return (T)x; }
+
+}  // namespace attn

@@ -1,0 +1,54 @@
+// Internal launcher interface between the C ABI (api.hip) and the kernels.
+// Every launcher assumes the problem has already been validated by the ABI
+// layer: pointers aligned and non-null where used, sizes within the limits
+// stated in include/attn.h, D in {16, 32, 64, 128}, B*H*Nq > 0 and Nk > 0.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+struct Problem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* m_out;  // optional [B*H*Nq]
+  float* l_out;  // optional [B*H*Nq]
+  int64_t B, H, Nq, Nk, D;
+  bool causal;
+  float scale;
+  DType dtype;
+  hipStream_t stream;
+};
+
+// Streaming prefill on bf16/f16 matrix cores (prefill_mfma.hip).
+hipError_t launch_prefill_mfma(const Problem& p);
+// Streaming prefill for FP32 inputs on the vector ALUs (prefill_f32.hip).
+hipError_t launch_prefill_f32(const Problem& p);
+
+// Split-key decode path (decode_splitk.hip): partial states per key split
+// into `scratch`, then a merge kernel on the same stream.
+struct DecodePlan {
+  int splits;           // key splits per query row
+  int keys_per_split;   // keys each split streams
+  size_t scratch_bytes; // partial (m, l, a[D]) states, FP32
+};
+DecodePlan plan_decode(const Problem& p);
+hipError_t launch_decode(const Problem& p, const DecodePlan& plan, float* scratch);
+
+// Nk == 0: out = 0, (m, l) = (-inf, 0) (misc.hip).
+hipError_t launch_fill_empty(const Problem& p);
+
+// Elementwise A1 merge of FP32 device arrays, natural-log units (misc.hip).
+hipError_t launch_merge_batch(const float* m1, const float* l1, const float* m2,
+                              const float* l2, float* m, float* l, int64_t n,
+                              hipStream_t stream);
+
+// Row count above which attn_fwd takes the prefill kernels.
+constexpr int64_t kDecodeMaxNq = 8;
+
+}  // namespace attn

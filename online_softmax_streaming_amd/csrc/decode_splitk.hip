@@ -1,0 +1,253 @@
+// Split-key decode path: few query rows per head, many keys.
+//
+// With Nq <= 8 a query tile of the prefill kernels would be mostly ghost
+// rows, and one workgroup per (b, h) cannot fill 256 CUs.  Instead each
+// query row's keys are cut into S splits.  This follows the wide-row split
+// softmax of the workshops page (split_softmax row of "Scope and
+// contracts") and its answer-key row A2: partial statistics per chunk, then
+// a rescaled merge, ordered by launching both kernels on one stream, with a
+// per-call scratch array.
+//
+//   kernel 1 (partial): workgroup (row, split) streams its keys, carrying
+//     (m, l, a) per lane group exactly as the prefill kernels do (answer-key
+//     row A3), folds the groups with the A1 merge, and writes the split's
+//     state (m, l, a[0..D)) to scratch.  Base-2 units.
+//   kernel 2 (combine): workgroup `row` folds the S partial states with the
+//     A1 merge (answer-key row A1), normalises and casts once.
+//
+// The path is bound by HBM bandwidth (each K/V byte is read once and used
+// for one multiply-add), so it runs on the vector ALUs: lanes read 16-byte
+// chunks, D/VEC lanes cover one key row, and each loop step keeps U rows
+// per lane group in flight.
+
+#include "attn_device.h"
+#include "attn_kernels.h"
+
+namespace attn {
+namespace {
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* m_out;
+  float* l_out;
+  float* part;  // [rows][S][D + 2]: m, l, a[D]
+  int H, Nq, Nk;
+  int S;
+  int kps;  // keys per split
+  float c;  // scale * log2(e)
+};
+
+constexpr int kThreads = 256;
+
+template <typename T> struct Vec16;
+template <> struct Vec16<__bf16> { typedef bf16x8 type; static constexpr int n = 8; };
+template <> struct Vec16<_Float16> { typedef f16x8 type; static constexpr int n = 8; };
+template <> struct Vec16<float> { typedef f32x4 type; static constexpr int n = 4; };
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) {
+  typedef typename Vec16<T>::type vec;
+  constexpr int VEC = Vec16<T>::n;
+  constexpr int LPR = D / VEC;          // lanes per key row
+  constexpr int G = kThreads / LPR;     // lane groups per workgroup
+  constexpr int U = 4;                  // key rows per group per step
+
+  __shared__ float sm[G], sl[G];
+  __shared__ float sa[G * D];
+
+  const int row = blockIdx.x;  // (b*H + h)*Nq + i
+  const int split = blockIdx.y;
+  const int Nq = a.Nq, Nk = a.Nk;
+  const int bh = row / Nq;
+  const int i = row - bh * Nq;
+  const int tid = threadIdx.x;
+  const int g = tid / LPR;
+  const int sub = tid - g * LPR;
+  const float c = a.c;
+
+  const T* __restrict__ Kh = static_cast<const T*>(a.k) + (int64_t)bh * Nk * D;
+  const T* __restrict__ Vh = static_cast<const T*>(a.v) + (int64_t)bh * Nk * D;
+
+  float qv[VEC];
+  {
+    const vec q = *reinterpret_cast<const vec*>(static_cast<const T*>(a.q) + (int64_t)row * D + sub * VEC);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) qv[e] = to_f32<T>(q[e]);
+  }
+
+  int kend = Nk;
+  if (CAUSAL) kend = min(Nk, i + (Nk - Nq) + 1);
+  const int kb = split * a.kps;
+  const int ke = min(kend, kb + a.kps);
+
+  float m_run = kNegInf, l_run = 0.f;
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+
+  for (int j = kb + g; j < ke; j += G * U) {
+    vec kv[U], vv[U];
+    bool in[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jj = j + u * G;
+      in[u] = jj < ke;
+      kv[u] = in[u] ? *reinterpret_cast<const vec*>(Kh + (int64_t)jj * D + sub * VEC) : vec{};
+      vv[u] = in[u] ? *reinterpret_cast<const vec*>(Vh + (int64_t)jj * D + sub * VEC) : vec{};
+    }
+    float s[U];
+    float mx = kNegInf;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) dot = __builtin_fmaf(qv[e], to_f32<T>(kv[u][e]), dot);
+#pragma unroll
+      for (int o = LPR / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+      // Rounded product kept apart from the later subtraction, so the
+      // largest score gives exactly 2^0 = 1.
+      s[u] = in[u] ? dot * c : kNegInf;
+      mx = fmaxf(mx, s[u]);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float ref = pinned_ref(m_new);
+    const float alpha = exp2_hw(m_run - ref);
+    float rs = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      s[u] = exp2_hw(s[u] - ref);
+      rs += s[u];
+    }
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      float x = acc[e] * alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) x = __builtin_fmaf(s[u], to_f32<T>(vv[u][e]), x);
+      acc[e] = x;
+    }
+    m_run = m_new;
+  }
+
+  // Fold the G lane-group states of this workgroup (A1 merge).
+  if (sub == 0) {
+    sm[g] = m_run;
+    sl[g] = l_run;
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) sa[g * D + sub * VEC + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    float M = kNegInf, L = 0.f, A = 0.f;
+    for (int gg = 0; gg < G; ++gg) {
+      const MergeWeights w = merge_weights_log2(M, sm[gg]);
+      L = L * w.w1 + sl[gg] * w.w2;
+      A = A * w.w1 + sa[gg * D + tid] * w.w2;
+      M = w.m;
+    }
+    float* dst = a.part + ((int64_t)row * a.S + split) * (D + 2);
+    dst[2 + tid] = A;
+    if (tid == 0) {
+      dst[0] = M;
+      dst[1] = L;
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* src = a.part + (int64_t)row * a.S * (D + 2);
+  float M = kNegInf, L = 0.f, A = 0.f;
+  for (int s = 0; s < a.S; ++s) {
+    const float* st = src + (int64_t)s * (D + 2);
+    const MergeWeights w = merge_weights_log2(M, st[0]);
+    L = L * w.w1 + st[1] * w.w2;
+    if (tid < D) A = A * w.w1 + st[2 + tid] * w.w2;
+    M = w.m;
+  }
+  if (tid < D) {
+    const float out = L > 0.f ? A / L : 0.f;
+    static_cast<T*>(a.o)[(int64_t)row * D + tid] = from_f32<T>(out);
+  }
+  if (tid == 0) {
+    if (a.m_out) a.m_out[row] = M * kLn2;
+    if (a.l_out) a.l_out[row] = L;
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_typed(const Problem& p, const DecodePlan& plan, float* scratch) {
+  DecodeArgs a;
+  a.q = p.q;
+  a.k = p.k;
+  a.v = p.v;
+  a.o = p.o;
+  a.m_out = p.m_out;
+  a.l_out = p.l_out;
+  a.part = scratch;
+  a.H = (int)p.H;
+  a.Nq = (int)p.Nq;
+  a.Nk = (int)p.Nk;
+  a.S = plan.splits;
+  a.kps = plan.keys_per_split;
+  a.c = p.scale * kLog2e;
+  const int64_t rows = p.B * p.H * p.Nq;
+  hipLaunchKernelGGL((decode_partial_kernel<T, D, CAUSAL>), dim3((unsigned)rows, plan.splits),
+                     dim3(kThreads), 0, p.stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)rows), dim3(128), 0, p.stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_d(const Problem& p, const DecodePlan& plan, float* scratch) {
+  return p.causal ? launch_typed<T, D, true>(p, plan, scratch)
+                  : launch_typed<T, D, false>(p, plan, scratch);
+}
+
+template <typename T>
+hipError_t launch_t(const Problem& p, const DecodePlan& plan, float* scratch) {
+  switch (p.D) {
+    case 16: return launch_d<T, 16>(p, plan, scratch);
+    case 32: return launch_d<T, 32>(p, plan, scratch);
+    case 64: return launch_d<T, 64>(p, plan, scratch);
+    case 128: return launch_d<T, 128>(p, plan, scratch);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+DecodePlan plan_decode(const Problem& p) {
+  // Aim for >= 4096 workgroups (16 per CU) so the HBM stream is deep enough,
+  // but give each split at least 256 keys so the merge stays cheap.
+  const int64_t rows = p.B * p.H * p.Nq;
+  const int64_t want = (4096 + rows - 1) / rows;
+  int64_t kps = (p.Nk + want - 1) / want;
+  if (kps < 256) kps = 256;
+  int64_t splits = (p.Nk + kps - 1) / kps;
+  if (splits < 1) splits = 1;
+  if (splits > 65535) {  // grid.y limit
+    splits = 65535;
+    kps = (p.Nk + splits - 1) / splits;
+  }
+  DecodePlan plan;
+  plan.splits = (int)splits;
+  plan.keys_per_split = (int)kps;
+  plan.scratch_bytes = (size_t)rows * (size_t)splits * (size_t)(p.D + 2) * sizeof(float);
+  return plan;
+}
+
+hipError_t launch_decode(const Problem& p, const DecodePlan& plan, float* scratch) {
+  if (p.dtype == DType::BF16) return launch_t<__bf16>(p, plan, scratch);
+  if (p.dtype == DType::F16) return launch_t<_Float16>(p, plan, scratch);
+  return launch_t<float>(p, plan, scratch);
+}
+
+}  // namespace attn

@@ -1,0 +1,174 @@
+// Streaming attention prefill for FP32 inputs, on the vector ALUs.
+//
+// Same contract and running-state algorithm as the matrix-core kernel
+// (workshops page, "Scope and contracts"; answer-key page, row A3), kept in
+// FP32 end to end: P is not rounded before P.V because the input type is
+// already FP32.  This path exists for FP32 accuracy (max abs error 1e-5
+// against the FP64 oracle), not for throughput: gfx950 has no FP32 matrix
+// instruction faster than its vector FMA path by enough to matter here.
+//
+// One workgroup = 128 threads = 128/TPQ query rows; a row's features are
+// split over TPQ threads (TPQ = 2 for D = 128, so a thread keeps at most 64
+// features of q and 64 of the running output in registers).  Key tiles of
+// 32 rows are staged in LDS and read by broadcast.
+
+#include "attn_device.h"
+#include "attn_kernels.h"
+
+namespace attn {
+namespace {
+
+struct F32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* m_out;
+  float* l_out;
+  int Nq, Nk;
+  int nqt;
+  float c;  // scale * log2(e)
+};
+
+constexpr int kThreads = 128;
+constexpr int kBNF = 32;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
+  constexpr int TPQ = D > 64 ? 2 : 1;
+  constexpr int DT = D / TPQ;
+  constexpr int QPB = kThreads / TPQ;
+  constexpr int BN = kBNF;
+
+  __shared__ __attribute__((aligned(16))) float Ks[BN * D];
+  __shared__ __attribute__((aligned(16))) float Vs[BN * D];
+
+  const int bh = blockIdx.x / a.nqt;
+  const int qt = blockIdx.x - bh * a.nqt;
+  const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
+  const float* __restrict__ Qh = a.q + (int64_t)bh * Nq * D;
+  const float* __restrict__ Kh = a.k + (int64_t)bh * Nk * D;
+  const float* __restrict__ Vh = a.v + (int64_t)bh * Nk * D;
+  float* __restrict__ Oh = a.o + (int64_t)bh * Nq * D;
+
+  const int tid = threadIdx.x;
+  const int part = tid % TPQ;
+  const int i0 = qt * QPB;
+  const int qrow = i0 + tid / TPQ;
+  const float c = a.c;
+
+  float q[DT], acc[DT];
+#pragma unroll
+  for (int d = 0; d < DT; ++d) {
+    q[d] = qrow < Nq ? Qh[(int64_t)qrow * D + part * DT + d] : 0.f;
+    acc[d] = 0.f;
+  }
+  float m_run = kNegInf, l_run = 0.f;
+
+  int kend = Nk;
+  if (CAUSAL) kend = min(Nk, min(i0 + QPB, Nq) + off);
+  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * BN;
+    // Stage the tile: 16-byte loads, rows past Nk zero.
+    for (int e = tid; e < BN * D / 4; e += kThreads) {
+      const int row = e / (D / 4), col = e - row * (D / 4);
+      const int j = j0 + row;
+      f32x4 kv = f32x4{}, vv = f32x4{};
+      if (j < Nk) {
+        kv = *reinterpret_cast<const f32x4*>(Kh + (int64_t)j * D + col * 4);
+        vv = *reinterpret_cast<const f32x4*>(Vh + (int64_t)j * D + col * 4);
+      }
+      *reinterpret_cast<f32x4*>(&Ks[row * D + col * 4]) = kv;
+      *reinterpret_cast<f32x4*>(&Vs[row * D + col * 4]) = vv;
+    }
+    __syncthreads();
+
+    float s[BN];
+    float mx = kNegInf;
+#pragma unroll
+    for (int jj = 0; jj < BN; ++jj) {
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) dot = __builtin_fmaf(q[d], Ks[jj * D + part * DT + d], dot);
+      if (TPQ == 2) dot += __shfl_xor(dot, 1);
+      const int j = j0 + jj;
+      const bool vis = j < Nk && (!CAUSAL || j <= qrow + off);
+      // Rounded product kept apart from the later subtraction, so the
+      // largest score gives exactly 2^0 = 1.
+      s[jj] = vis ? dot * c : kNegInf;
+      mx = fmaxf(mx, s[jj]);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float ref = pinned_ref(m_new);
+    const float alpha = exp2_hw(m_run - ref);
+    float rs = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < BN; ++jj) {
+      s[jj] = exp2_hw(s[jj] - ref);
+      rs += s[jj];
+    }
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      float x = acc[d] * alpha;
+#pragma unroll
+      for (int jj = 0; jj < BN; ++jj) x = __builtin_fmaf(s[jj], Vs[jj * D + part * DT + d], x);
+      acc[d] = x;
+    }
+    m_run = m_new;
+    __syncthreads();
+  }
+
+  if (qrow < Nq) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) Oh[(int64_t)qrow * D + part * DT + d] = acc[d] * inv;
+    if (part == 0) {
+      const int64_t row = (int64_t)bh * Nq + qrow;
+      if (a.m_out) a.m_out[row] = m_run * kLn2;
+      if (a.l_out) a.l_out[row] = l_run;
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_typed(const Problem& p) {
+  constexpr int TPQ = D > 64 ? 2 : 1;
+  constexpr int QPB = kThreads / TPQ;
+  F32Args a;
+  a.q = static_cast<const float*>(p.q);
+  a.k = static_cast<const float*>(p.k);
+  a.v = static_cast<const float*>(p.v);
+  a.o = static_cast<float*>(p.o);
+  a.m_out = p.m_out;
+  a.l_out = p.l_out;
+  a.Nq = (int)p.Nq;
+  a.Nk = (int)p.Nk;
+  a.nqt = (int)((p.Nq + QPB - 1) / QPB);
+  a.c = p.scale * kLog2e;
+  const int64_t grid = p.B * p.H * a.nqt;
+  hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     p.stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const Problem& p) {
+  return p.causal ? launch_typed<D, true>(p) : launch_typed<D, false>(p);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_f32(const Problem& p) {
+  switch (p.D) {
+    case 16: return launch_d<16>(p);
+    case 32: return launch_d<32>(p);
+    case 64: return launch_d<64>(p);
+    case 128: return launch_d<128>(p);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace attn

@@ -1,0 +1,96 @@
+"""Seeded synthetic workloads: shapes and input generators.
+
+Holds none of the attention arithmetic; it only names the workloads and
+draws their inputs, so both the HIP path and the oracle can be fed the same
+tensors.  Recipe: Q, K, V ~ N(0, 1) as float32 from one seeded torch
+generator, drawn in the order Q, K, V, then rounded to the workload's dtype.
+The ragged workload adds ``k_ramp * j`` to every element of key row j (a
+rising key offset pushes the running max up tile after tile).
+"""
+
+import dataclasses
+
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    D: int
+    dtype: str
+    causal: bool
+    k_ramp: float = 0.0
+
+    @property
+    def torch_dtype(self):
+        return DTYPES[self.dtype]
+
+    def visible_pairs(self):
+        """Query-key pairs with a visible key, summed over (B, H)."""
+        if not self.causal:
+            per_head = self.Nq * self.Nk
+        else:
+            off = self.Nk - self.Nq
+            per_head = 0
+            # rows i see min(Nk, max(0, i + off + 1)) keys
+            lo = max(0, -off)                     # first row that sees a key
+            full = max(lo, min(self.Nq, self.Nk - off))  # first row that sees all Nk keys
+            n = full - lo
+            # rows lo..full-1 see i + off + 1 keys: arithmetic series
+            per_head += n * (lo + off + 1) + n * (n - 1) // 2
+            per_head += (self.Nq - full) * self.Nk
+        return self.B * self.H * per_head
+
+    def flops(self):
+        """Algorithmic FLOP: 2*D for Q.K^T plus 2*D for P.V per visible pair."""
+        return 4 * self.D * self.visible_pairs()
+
+    def bytes(self):
+        """Algorithmic HBM bytes: Q, K, V read once and out written once."""
+        el = torch.finfo(self.torch_dtype).bits // 8
+        return el * self.B * self.H * self.D * (2 * self.Nq + 2 * self.Nk)
+
+
+WORKLOADS = {w.name: w for w in [
+    Workload("tiny_f32", 1, 1, 128, 128, 64, "f32", False),
+    Workload("small_causal_bf16", 2, 4, 1024, 1024, 64, "bf16", True),
+    Workload("headline_causal_bf16", 4, 16, 4096, 4096, 128, "bf16", True),
+    Workload("headline_noncausal_bf16", 4, 16, 4096, 4096, 128, "bf16", False),
+    Workload("ragged_causal_f16", 3, 8, 4099, 4099, 64, "f16", True, 0.02),
+    Workload("ragged_noncausal_f16", 3, 8, 4099, 4099, 64, "f16", False, 0.02),
+    Workload("ragged_nk1_f16", 3, 8, 4099, 1, 64, "f16", False, 0.02),
+    Workload("ragged_n1_causal_f16", 3, 8, 1, 1, 64, "f16", True, 0.02),
+    Workload("ragged_b0_f16", 0, 8, 4099, 4099, 64, "f16", True, 0.02),
+    Workload("long_causal_bf16", 1, 32, 16384, 16384, 128, "bf16", True),
+    Workload("decode_bf16", 16, 32, 1, 32768, 128, "bf16", False),
+]}
+
+
+def make_qkv(w, seed=0, device="cpu"):
+    """Q, K, V for workload ``w``: N(0, 1) float32 from ``seed``, order Q, K, V,
+    key ramp added, then rounded to the workload dtype on ``device``."""
+    gen_device = "cpu" if str(device) == "cpu" else device
+    g = torch.Generator(device=gen_device)
+    g.manual_seed(seed)
+    shape_q = (w.B, w.H, w.Nq, w.D)
+    shape_k = (w.B, w.H, w.Nk, w.D)
+    q = torch.randn(shape_q, generator=g, dtype=torch.float32, device=gen_device)
+    k = torch.randn(shape_k, generator=g, dtype=torch.float32, device=gen_device)
+    v = torch.randn(shape_k, generator=g, dtype=torch.float32, device=gen_device)
+    if w.k_ramp:
+        ramp = w.k_ramp * torch.arange(w.Nk, dtype=torch.float32, device=gen_device)
+        k = k + ramp[:, None]
+    dt = w.torch_dtype
+    return (q.to(device=device, dtype=dt), k.to(device=device, dtype=dt),
+            v.to(device=device, dtype=dt))
+
+
+def random_qkv(B, H, Nq, Nk, D, dtype, seed=0, device="cpu", k_ramp=0.0):
+    """Same recipe for an ad-hoc shape."""
+    return make_qkv(Workload("adhoc", B, H, Nq, Nk, D, dtype, False, k_ramp), seed, device)

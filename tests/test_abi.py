@@ -1,0 +1,164 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every symbol include/attn.h declares, reject
+bad arguments before touching any device, and compute the host A1 merge to
+the oracle's values.  None of these calls launches a kernel.
+"""
+
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import online_merge as oracle_merge
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def attn():
+    from online_softmax_streaming_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from online_softmax_streaming_amd import build
+        build.build()
+    import online_softmax_streaming_amd as m
+    return m
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"ATTN_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_boundary():
+    names = set(_declared_symbols())
+    assert {"attn_fwd", "attn_fwd_stats", "online_merge", "online_merge_batch",
+            "attn_strerror", "attn_last_error"} <= names
+
+
+def test_library_exports_every_declared_symbol(attn):
+    import subprocess
+    from online_softmax_streaming_amd import _lib
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared_symbols():
+        assert name in exported, name
+        assert hasattr(_lib.lib(), name)
+    # Only the C ABI is exported.
+    assert exported == set(_declared_symbols())
+
+
+def test_library_is_a_gfx950_build(attn):
+    from online_softmax_streaming_amd import _lib
+    blob = open(_lib.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_strerror(attn):
+    assert attn.attn_strerror(0) == "success"
+    assert attn.attn_strerror(1) == "invalid argument"
+    assert attn.attn_strerror(2) == "unsupported configuration"
+    assert attn.attn_strerror(3) == "HIP runtime error"
+    assert attn.attn_strerror(99) == "unknown status code"
+
+
+def test_host_merge_worked_example(attn):
+    # Answer-key page, worked answer A1.
+    m, l = attn.online_merge(2.0, 2.0, 4.0, 1.0)
+    assert m == 4.0
+    assert abs(l - (1 + 2 * math.exp(-2))) <= 4e-16
+
+
+def test_host_merge_empty_cases(attn):
+    inf = float("inf")
+    assert attn.online_merge(-inf, 0.0, -inf, 0.0) == (-inf, 0.0)
+    assert attn.online_merge(1.5, 3.0, -inf, 0.0) == (1.5, 3.0)
+    assert attn.online_merge(-inf, 0.0, -7.0, 0.25) == (-7.0, 0.25)
+
+
+def test_host_merge_matches_oracle(attn):
+    rng = np.random.default_rng(0)
+    for _ in range(500):
+        m1, m2 = rng.normal(size=2) * 20
+        l1, l2 = rng.uniform(0, 100, size=2)
+        if rng.uniform() < 0.1:
+            m1, l1 = -math.inf, 0.0
+        got = attn.online_merge(m1, l1, m2, l2)
+        want = oracle_merge(m1, l1, m2, l2)
+        assert got[0] == want[0]
+        assert abs(got[1] - want[1]) <= 1e-15 * max(1.0, want[1])
+
+
+@pytest.mark.parametrize("args", [
+    (float("nan"), 1.0, 0.0, 1.0),
+    (float("inf"), 1.0, 0.0, 1.0),
+    (0.0, -1.0, 0.0, 1.0),
+    (0.0, 1.0, 0.0, float("nan")),
+    (0.0, float("inf"), 0.0, 1.0),
+])
+def test_host_merge_rejects_bad_states(attn, args):
+    with pytest.raises(attn.AttnError) as e:
+        attn.online_merge(*args)
+    assert e.value.code == attn.ATTN_E_INVALID
+
+
+def _raw(attn, **kw):
+    args = dict(q_ptr=0x1000, k_ptr=0x2000000, v_ptr=0x4000000, out_ptr=0x8000000, b=1, h=1,
+                nq=16, nk=16, d=64, causal=0, scale=0.125, dtype=attn.ATTN_BF16)
+    args.update(kw)
+    return attn.attn_fwd_raw(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), 1),
+    (dict(causal=2), 1),
+    (dict(b=-1), 1),
+    (dict(nk=-3), 1),
+    (dict(d=0), 1),
+    (dict(scale=0.0), 1),
+    (dict(scale=-0.5), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(scale=float("inf")), 1),
+    (dict(d=48), 2),
+    (dict(d=256), 2),
+    (dict(q_ptr=0), 1),
+    (dict(out_ptr=0), 1),
+    (dict(k_ptr=0), 1),
+    (dict(q_ptr=0x1008), 1),            # misaligned
+    (dict(out_ptr=0x1000 + 1024), 1),   # out overlaps Q
+    (dict(nq=1 << 31), 1),
+    (dict(nk=(1 << 31) // 64), 1),      # Nk*D reaches 2^31
+    (dict(b=1 << 16, h=1 << 16), 1),    # B*H reaches 2^32
+])
+def test_attn_fwd_rejects_bad_arguments(attn, kw, code):
+    assert _raw(attn, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(b=0), dict(h=0), dict(nq=0),
+                                dict(b=0, q_ptr=0, k_ptr=0, v_ptr=0, out_ptr=0)])
+def test_attn_fwd_empty_is_a_noop(attn, kw):
+    # B, H or Nq == 0 returns before any device work, whatever the pointers.
+    assert _raw(attn, **kw) == 0
+
+
+def test_last_error_text(attn):
+    from online_softmax_streaming_amd import _lib
+    assert _raw(attn, d=48) == 2
+    assert "D=48" in _lib.lib().attn_last_error().decode()
+    assert _raw(attn, scale=-1.0) == 1
+    assert "scale" in _lib.lib().attn_last_error().decode()
+
+
+def test_merge_batch_rejects_bad_sizes(attn):
+    from online_softmax_streaming_amd import _lib
+    L = _lib.lib()
+    import ctypes
+    p = ctypes.c_void_p(0x1000)
+    assert L.online_merge_batch(p, p, p, p, p, p, -1, None) == 1
+    assert L.online_merge_batch(p, p, p, p, p, p, 0, None) == 0
+    assert L.online_merge_batch(None, p, p, p, p, p, 4, None) == 1
+    assert L.online_merge_batch(ctypes.c_void_p(0x1001), p, p, p, p, p, 4, None) == 1

@@ -4,7 +4,7 @@
 // ("Intermediate and advanced kernel workshops", section "Scope and
 // contracts"), batched over (B, H): each query row carries a running max m,
 // running sum l and unnormalised output a across key tiles, rescaling l and
-// a together when m rises (answer-key page, row A3), and one score tile is
+// a together when m moves (answer-key page, row A3), and one score tile is
 // alive at a time.  Masked or padded scores are -inf before the max and add
 // 0 to the sums, and rows with nothing visible are pinned at reference 0
 // ("Kernel Notes & Checklist", gotchas ledger).
@@ -12,14 +12,23 @@
 // Work decomposition (one workgroup = NW waves = 32*NW query rows):
 //   * Each wave owns 32 query rows.  Its Q rows stay in registers for the
 //     whole kernel as the B operand of v_mfma_f32_32x32x16_{bf16,f16}.
-//   * Key tiles of BN = 64 rows are staged in LDS, double-buffered: K
-//     row-major, V transposed (V^T[d][key]) so the P.V product can read its
-//     key-contiguous operand with one 16-byte LDS read.
+//   * Key tiles of BN = 64 rows of K and V are staged in LDS, double-buffered:
+//     buffer loads for tile t+1 are in flight while tile t is computed, and
+//     rows past Nk fall outside the buffer's range and arrive as zeros, so
+//     the ragged tail needs no branch.  Both tiles are stored row-major with
+//     an XOR swizzle of 16-byte chunks that makes every LDS read below
+//     bank-conflict free.
 //   * S^T = K Q^T is formed per 32-key block, so each lane owns one query
-//     column: the row max/sum over keys is in-lane plus one exchange between
-//     the two half-waves.  P^T stays in registers as the B operand of
-//     O^T += V^T P^T, again with one query per lane, so the rescale by
-//     alpha is a per-lane scalar.
+//     column: the row max over keys is in-lane plus one exchange between the
+//     two half-waves.  P^T stays in registers as the B operand of
+//     O^T += V^T P^T, again one query per lane, so the rescale is a per-lane
+//     scalar.  The V^T operand (8 keys of one feature per lane) is read from
+//     the row-major V tile with the LDS transpose read ds_read_b64_tr_b16.
+//   * The reference max is refreshed only when a row's max rises by more
+//     than 8 in base-2 units; until then exponentials may reach 2^8, which
+//     FP32 accumulators and bf16/f16 weights carry without loss.  Skipping
+//     the refresh removes the O rescale from most tiles.  The exact row max
+//     is tracked separately for the returned row state.
 //   * Causal: a query tile visits only key tiles that hold a visible key
 //     (the pages' answer visits every tile); inside a tile a wave whose rows
 //     see none of its keys skips the math, and masks are applied only on
@@ -31,6 +40,11 @@
 // A and B use the same k slots, so the contraction needs no assumption
 // about which k-slot the hardware gives each half-wave; only the C layout
 // is relied on, and any other C layout fails the parity tests.
+//
+// ds_read_b64_tr_b16, per group of 16 lanes: if lane r addresses 4 halves
+// M[r][0..3], lane i receives M[4e + i/4][i%4] for e = 0..3.
+
+#include <type_traits>
 
 #include "attn_device.h"
 #include "attn_kernels.h"
@@ -38,9 +52,14 @@
 namespace attn {
 namespace {
 
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 template <typename T> struct Mfma;
 template <> struct Mfma<__bf16> {
   typedef bf16x8 vec8;
+  typedef __bf16 vec4 __attribute__((ext_vector_type(4)));
   typedef __bf16 vec2 __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -53,6 +72,7 @@ template <> struct Mfma<__bf16> {
 };
 template <> struct Mfma<_Float16> {
   typedef f16x8 vec8;
+  typedef _Float16 vec4 __attribute__((ext_vector_type(4)));
   typedef _Float16 vec2 __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -77,27 +97,44 @@ struct PrefillArgs {
   float c;      // scale * log2(e)
 };
 
-constexpr int kBN = 64;  // keys per tile
+constexpr int kBN = 64;              // keys per tile
+constexpr float kRefreshGap = 8.0f;  // base-2 units; see the file comment
+
+// Tile geometry: rows of D halves (2*D bytes), 16-byte chunks XOR-swizzled by
+// row so that 16 lanes reading 16 rows (K) or 4 rows x 32 bytes (V, transpose
+// read) touch every LDS bank equally.
+template <int D> struct Geo {
+  static constexpr int CPR = D / 8;                     // chunks per row
+  static constexpr int RPL = CPR >= 16 ? 1 : 16 / CPR;  // rows per 256 bytes
+  static __device__ __forceinline__ int swz(int row) { return (2 * (row / RPL)) & (CPR - 1); }
+  static __device__ __forceinline__ int off(int row, int chunk) {
+    return row * (2 * D) + ((chunk ^ swz(row)) << 4);
+  }
+};
+
+// x from lane l ^ 32 (the other half-wave).
+__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32); }
 
 template <typename T, int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_mfma_kernel(PrefillArgs a) {
   typedef typename Mfma<T>::vec8 vec8;
-  constexpr int NT = NW * 64;
+  typedef typename Mfma<T>::vec4 vec4;
+  typedef typename Mfma<T>::vec2 vec2;
+  typedef Geo<D> G;
   constexpr int BM = 32 * NW;
   constexpr int BN = kBN;
-  constexpr int DP = D < 32 ? 32 : D;   // O^T rows, padded to one MFMA block
-  constexpr int KC = D / 16;            // k-chunks of Q.K^T
-  constexpr int NB = DP / 32;           // 32-row blocks of O^T
-  constexpr int KSTR = D + 8;           // LDS row stride of K (elements)
-  constexpr int VSTR = BN + 8;          // LDS row stride of V^T (elements)
-  constexpr int DV = D / 8;             // 16-byte chunks per row
-  constexpr int KCHUNKS = BN * DV;      // 16-byte chunks per K tile
-  constexpr int KPT = (KCHUNKS + NT - 1) / NT;
-  constexpr int VBLK = (BN / 4) * DV;   // 4-key x 8-column blocks per V tile
-  constexpr int VPT = (VBLK + NT - 1) / NT;
+  constexpr int DP = D < 32 ? 32 : D;  // O^T rows, padded to one MFMA block
+  constexpr int KC = D / 16;           // k-chunks of Q.K^T
+  constexpr int NB = DP / 32;          // 32-row blocks of O^T
+  constexpr int NT = NW * 64;          // threads per workgroup
+  constexpr int TILE = BN * D * 2;     // bytes of one K or V tile
+  // Moving 32 rows (K blocks) or 8 rows (V halves) keeps each row's swizzle,
+  // so those steps are plain constant offsets.
+  static_assert((2 * 32 / G::RPL) % G::CPR == 0, "K block step must keep the swizzle");
+  static_assert((2 * 8 / G::RPL) % G::CPR == 0, "V row step must keep the swizzle");
 
-  __shared__ __attribute__((aligned(16))) T Ks[2][BN * KSTR];
-  __shared__ __attribute__((aligned(16))) T Vt[2][DP * VSTR];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][TILE];  // [buf][K, V]
 
   // Workgroup -> (head, query tile).  Consecutive workgroup ids land on
   // different XCDs (round-robin over 8); regroup them so each XCD walks a
@@ -112,13 +149,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a) {
 
   const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
   const T* __restrict__ Qh = static_cast<const T*>(a.q) + (int64_t)bh * Nq * D;
-  const T* __restrict__ Kh = static_cast<const T*>(a.k) + (int64_t)bh * Nk * D;
-  const T* __restrict__ Vh = static_cast<const T*>(a.v) + (int64_t)bh * Nk * D;
+  const T* Kh = static_cast<const T*>(a.k) + (int64_t)bh * Nk * D;
+  const T* Vh = static_cast<const T*>(a.v) + (int64_t)bh * Nk * D;
   T* __restrict__ Oh = static_cast<T*>(a.o) + (int64_t)bh * Nq * D;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h32 = lane >> 5;
   const int l32 = lane & 31;
   const int i0 = qt * BM;
@@ -131,11 +168,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a) {
   vec8 qf[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
-    if (qrow < Nq) {
-      qf[kc] = *reinterpret_cast<const vec8*>(Qh + (int64_t)qrow * D + kc * 16 + h32 * 8);
-    } else {
-      qf[kc] = vec8{};
-    }
+    qf[kc] = qrow < Nq
+                 ? *reinterpret_cast<const vec8*>(Qh + (int64_t)qrow * D + kc * 16 + h32 * 8)
+                 : vec8{};
   }
 
   // Key range that holds a visible key for some real row of this tile.
@@ -143,99 +178,90 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a) {
   if (CAUSAL) kend = min(Nk, min(i0 + BM, Nq) + off);
   const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
 
-  float m_run = kNegInf;  // running max, base-2 units
-  float l_run = 0.f;      // this half-wave's share of the running sum
+  // Buffer resources over this head's K and V: offsets at or past Nk rows
+  // are out of range and read as zero.
+  const uint32_t kv_bytes = (uint32_t)Nk * (uint32_t)(2 * D);
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(Kh), 0, (int)kv_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(Vh), 0, (int)kv_bytes, 0x00020000);
+
+  // Per-lane LDS byte offsets, loop invariant.
+  int koff[KC];  // K fragment of k-chunk kc for key l32 (+32 rows for block 1)
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) koff[kc] = G::off(l32, 2 * kc + h32);
+  int voff[NB];  // transpose-read address: key 4*h32 + i/4, features 4*(i%4).. of block n
+  {
+    const int i = lane & 15;
+    const int row = 4 * h32 + (i >> 2);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      int col = 16 * ((lane >> 4) & 1) + 32 * n + 4 * (i & 3);
+      if (col >= D) col -= D;  // D = 16: O^T rows 16..31 are computed, then discarded
+      voff[n] = G::off(row, col >> 3) + ((col & 7) << 1);
+    }
+  }
+
+  float m_run = kNegInf;   // reference max for the exponentials, base-2 units
+  float m_true = kNegInf;  // exact running max, base-2 units
+  float l_run = 0.f;       // this half-wave's share of the running sum
   f32x16 acc[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) acc[n] = f32x16{};
 
-  if (D < 32) {
-    // O^T rows D..31 are computed from these V^T rows and then discarded;
-    // zero them once so they hold no stale LDS contents.
-    for (int e = tid; e < 2 * (DP - D) * VSTR; e += NT) {
-      const int b = e / ((DP - D) * VSTR);
-      const int r = e - b * (DP - D) * VSTR;
-      Vt[b][D * VSTR + r] = T(0.f);
-    }
-  }
-
-  vec8 kreg[KPT];
-  vec8 vreg[VPT][4];
-
+  // Tile staging: each thread moves NPT 16-byte slots of K and of V per tile,
+  // HBM -> registers (buffer loads: rows past Nk are out of range and read
+  // as zero) -> LDS.  LDS slot s holds chunk (s % CPR) ^ swz(row) of row
+  // s / CPR, so consecutive lanes write consecutive 16 bytes and read a
+  // permutation of one row's chunks (still one coalesced row per 16 lanes
+  // for D = 128).
+  constexpr int NSLOT = TILE / 16;
+  constexpr int NPT = (NSLOT + NT - 1) / NT;
+  u32x4 kreg[NPT], vreg[NPT];
   auto load_tile = [&](int j0) {
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int ch = tid + u * NT;
-      if (KCHUNKS % NT == 0 || ch < KCHUNKS) {
-        const int row = ch / DV, col = ch - row * DV;
-        const int j = j0 + row;
-        kreg[u] = j < Nk ? *reinterpret_cast<const vec8*>(Kh + (int64_t)j * D + col * 8) : vec8{};
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int b = tid + u * NT;
-      if (VBLK % NT == 0 || b < VBLK) {
-        const int kq = b / DV, dc = b - kq * DV;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = j0 + kq * 4 + i;
-          vreg[u][i] = j < Nk ? *reinterpret_cast<const vec8*>(Vh + (int64_t)j * D + dc * 8) : vec8{};
-        }
+    for (int u = 0; u < NPT; ++u) {
+      const int sl = tid + u * NT;
+      if (NSLOT % NT == 0 || sl < NSLOT) {
+        const int row = sl / G::CPR;
+        const int chunk = (sl % G::CPR) ^ G::swz(row);
+        const int j = min(j0 + row, Nk);  // rows past Nk: out of range, read as 0
+        const uint32_t vo = (uint32_t)j * (uint32_t)(2 * D) + (uint32_t)(chunk << 4);
+        kreg[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)vo, 0, 0);
+        vreg[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)vo, 0, 0);
       }
     }
   };
-
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int ch = tid + u * NT;
-      if (KCHUNKS % NT == 0 || ch < KCHUNKS) {
-        const int row = ch / DV, col = ch - row * DV;
-        *reinterpret_cast<vec8*>(&Ks[buf][row * KSTR + col * 8]) = kreg[u];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int b = tid + u * NT;
-      if (VBLK % NT == 0 || b < VBLK) {
-        const int kq = b / DV, dc = b - kq * DV;
-        // Keys 4kq..4kq+3 go to 4 adjacent V^T columns.  Within each group
-        // of 16 keys, key 8a + 4b + c sits at column 8b + 4a + c: then the
-        // 8 keys one lane feeds to one P.V MFMA (see compute) are adjacent.
-        const int pos = (kq >> 2) * 16 + (kq & 1) * 8 + ((kq >> 1) & 1) * 4;
-        const u32x4 r0 = __builtin_bit_cast(u32x4, vreg[u][0]);
-        const u32x4 r1 = __builtin_bit_cast(u32x4, vreg[u][1]);
-        const u32x4 r2 = __builtin_bit_cast(u32x4, vreg[u][2]);
-        const u32x4 r3 = __builtin_bit_cast(u32x4, vreg[u][3]);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          // Feature 2w: low halves; feature 2w+1: high halves.
-          u32x2 lo, hi;
-          lo.x = __builtin_amdgcn_perm(r1[w], r0[w], 0x05040100u);
-          lo.y = __builtin_amdgcn_perm(r3[w], r2[w], 0x05040100u);
-          hi.x = __builtin_amdgcn_perm(r1[w], r0[w], 0x07060302u);
-          hi.y = __builtin_amdgcn_perm(r3[w], r2[w], 0x07060302u);
-          *reinterpret_cast<u32x2*>(&Vt[buf][(dc * 8 + 2 * w) * VSTR + pos]) = lo;
-          *reinterpret_cast<u32x2*>(&Vt[buf][(dc * 8 + 2 * w + 1) * VSTR + pos]) = hi;
-        }
+    for (int u = 0; u < NPT; ++u) {
+      const int sl = tid + u * NT;
+      if (NSLOT % NT == 0 || sl < NSLOT) {
+        *reinterpret_cast<u32x4*>(&smem[buf][0][sl * 16]) = kreg[u];
+        *reinterpret_cast<u32x4*>(&smem[buf][1][sl * 16]) = vreg[u];
       }
     }
   };
 
-  auto compute = [&](int buf, int j0, bool need_mask) {
-    const T* ks = Ks[buf];
-    const T* vt = Vt[buf];
-    // S^T = K Q^T for two 32-key blocks.
+  auto compute = [&](auto bufc, int j0, bool need_mask) {
+    constexpr int buf = decltype(bufc)::value;
+    const unsigned char* kt = &smem[buf][0][0];
+    const unsigned char* vt = &smem[buf][1][0];
+
+    // S^T = K Q^T for two 32-key blocks; every K fragment of the tile is
+    // requested before the first MFMA so LDS latency overlaps the math.
+    vec8 kf[BN / 32][KC];
+#pragma unroll
+    for (int mb = 0; mb < BN / 32; ++mb)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        kf[mb][kc] = *reinterpret_cast<const vec8*>(kt + koff[kc] + mb * 32 * 2 * D);
     f32x16 s[BN / 32];
 #pragma unroll
     for (int mb = 0; mb < BN / 32; ++mb) {
       s[mb] = f32x16{};
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const vec8 ka = *reinterpret_cast<const vec8*>(ks + (mb * 32 + l32) * KSTR + kc * 16 + h32 * 8);
-        s[mb] = Mfma<T>::mma(ka, qf[kc], s[mb]);
-      }
+      for (int kc = 0; kc < KC; ++kc) s[mb] = Mfma<T>::mma(kf[mb][kc], qf[kc], s[mb]);
     }
     if (need_mask) {
 #pragma unroll
@@ -248,16 +274,25 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a) {
         }
       }
     }
-    // Row max over this tile: in-lane, then across the two half-waves.
+    // Tile max of this row: in-lane, then across the two half-waves.
     float mx = s[0][0];
 #pragma unroll
     for (int mb = 0; mb < BN / 32; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c);
-    const float ref = pinned_ref(m_new);
-    const float alpha = exp2_hw(m_run - ref);
+    mx = fmaxf(mx, other_half(mx));
+    const float m_tile = mx * c;  // -inf when nothing in the tile is visible
+    m_true = fmaxf(m_true, m_tile);
+    const bool refresh = m_tile > m_run + kRefreshGap;
+    if (__builtin_amdgcn_ballot_w64(refresh)) {
+      const float m_new = refresh ? m_tile : m_run;
+      const float alpha = exp2_hw(m_run - pinned_ref(m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < NB; ++n) acc[n] *= alpha;
+      m_run = m_new;
+    }
+    const float ref = pinned_ref(m_run);
 #pragma unroll
     for (int mb = 0; mb < BN / 32; ++mb)
 #pragma unroll
@@ -266,7 +301,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a) {
     // P^T rounded to the input type: the B operand of O^T += V^T P^T.  The
     // row sum adds the same rounded weights, so the normalisation matches
     // the numerator exactly (one visible key gives weight 1 and out = V).
-    typedef typename Mfma<T>::vec2 vec2;
     vec8 pf[BN / 16];
     float rs = 0.f;
 #pragma unroll
@@ -276,18 +310,28 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) rs = Mfma<T>::sum2(vec2{pf[c2][2 * e], pf[c2][2 * e + 1]}, rs);
     }
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int n = 0; n < NB; ++n) acc[n] *= alpha;
-    m_run = m_new;
+    l_run += rs;
+
+    // O^T += V^T P^T.  Slot e (0..3) of the first transpose read is key
+    // 16*c2 + 4*h32 + e, of the second key 16*c2 + 8 + 4*h32 + e: the keys
+    // that registers 8*(c2&1) + 0..7 of S^T block c2/2 hold.
+    vec8 vf[NB][BN / 16];
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
 #pragma unroll
       for (int c2 = 0; c2 < BN / 16; ++c2) {
-        const vec8 va = *reinterpret_cast<const vec8*>(vt + (n * 32 + l32) * VSTR + c2 * 16 + h32 * 8);
-        acc[n] = Mfma<T>::mma(va, pf[c2], acc[n]);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            LDS_PTR(s16x4, vt + voff[n] + (16 * c2) * 2 * D));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            LDS_PTR(s16x4, vt + voff[n] + (16 * c2 + 8) * 2 * D));
+        vf[n][c2] =
+            __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int c2 = 0; c2 < BN / 16; ++c2) acc[n] = Mfma<T>::mma(vf[n][c2], pf[c2], acc[n]);
   };
 
   if (ntiles > 0) {
@@ -295,22 +339,28 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a) {
     store_tile(0);
     __syncthreads();
     const int q_last = min(qw0 + 32, Nq) - 1;  // last real row of this wave
-    for (int t = 0; t < ntiles; ++t) {
+    auto step = [&](auto bufc, int t) {
+      constexpr int buf = decltype(bufc)::value;
       const int j0 = t * BN;
       const bool more = t + 1 < ntiles;
-      if (more) load_tile(j0 + BN);
+      if (more) load_tile(j0 + BN);  // in flight while this tile is computed
       const bool active = qw0 < Nq && (!CAUSAL || j0 <= q_last + off);
       if (active) {
         const bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + off);
-        compute(t & 1, j0, need_mask);
+        compute(bufc, j0, need_mask);
       }
-      if (more) store_tile((t + 1) & 1);
+      // Buffer buf^1 was last read in step t-1, before that step's barrier.
+      if (more) store_tile(buf ^ 1);
       __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
     }
   }
 
   // Epilogue: join the two half-wave sums, normalise, one cast, store.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = l_run + other_half(l_run);
   if (qrow < Nq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     T* orow = Oh + (int64_t)qrow * D;
@@ -320,18 +370,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int d0 = n * 32 + g * 8 + h32 * 4;
         if (d0 < D) {
-          typedef T t4 __attribute__((ext_vector_type(4)));
-          t4 o4;
+          vec4 o4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) o4[e] = from_f32<T>(acc[n][g * 4 + e] * inv);
-          *reinterpret_cast<t4*>(orow + d0) = o4;
+          *reinterpret_cast<vec4*>(orow + d0) = o4;
         }
       }
     }
     if (h32 == 0) {
+      // Row state relative to the exact max: sum exp = l * e^m.
       const int64_t row = (int64_t)bh * Nq + qrow;
-      if (a.m_out) a.m_out[row] = m_run * kLn2;
-      if (a.l_out) a.l_out[row] = l_tot;
+      const float to_true = m_true == kNegInf ? 0.f : exp2_hw(m_run - m_true);
+      if (a.m_out) a.m_out[row] = m_true * kLn2;
+      if (a.l_out) a.l_out[row] = l_tot * to_true;
     }
   }
 }
@@ -354,14 +405,16 @@ hipError_t launch_typed(const Problem& p) {
   const int64_t grid = (total + 7) / 8 * 8;
   a.per_xcd = (int)(grid / 8);
   a.c = p.scale * kLog2e;
-  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64),
-                     0, p.stream, a);
+  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, NW, CAUSAL>), dim3((unsigned)grid),
+                     dim3(NW * 64), 0, p.stream, a);
   return hipGetLastError();
 }
 
+constexpr int kWaves = 8;
+
 template <typename T, int D>
 hipError_t launch_d(const Problem& p) {
-  return p.causal ? launch_typed<T, D, 4, true>(p) : launch_typed<T, D, 4, false>(p);
+  return p.causal ? launch_typed<T, D, kWaves, true>(p) : launch_typed<T, D, kWaves, false>(p);
 }
 
 template <typename T>

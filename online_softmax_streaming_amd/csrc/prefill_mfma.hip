@@ -100,15 +100,30 @@ struct PrefillArgs {
 constexpr int kBN = 64;              // keys per tile
 constexpr float kRefreshGap = 8.0f;  // base-2 units; see the file comment
 
-// Tile geometry: rows of D halves (2*D bytes), 16-byte chunks XOR-swizzled by
-// row so that 16 lanes reading 16 rows (K) or 4 rows x 32 bytes (V, transpose
-// read) touch every LDS bank equally.
+// Tile geometry: rows of D halves (2*D bytes) in 16-byte chunks, chunk c of
+// row r stored at position c ^ swz(r).  LDS serves 256 bytes per pass: 16
+// lanes of a 16-byte read, 32 lanes of an 8-byte read.  The swizzle puts
+// the 16 rows of one K-fragment pass (same chunk, consecutive rows) and the
+// 4 rows x 2 feature groups of one V transpose-read pass on distinct banks.
 template <int D> struct Geo {
   static constexpr int CPR = D / 8;                     // chunks per row
   static constexpr int RPL = CPR >= 16 ? 1 : 16 / CPR;  // rows per 256 bytes
-  static __device__ __forceinline__ int swz(int row) { return (2 * (row / RPL)) & (CPR - 1); }
+  static constexpr __host__ __device__ int swz(int row) {
+    const int u = row / RPL;  // 256-byte line of the row
+    return CPR == 16 ? 4 * (u & 3) + ((u >> 2) & 3)
+         : CPR == 8  ? 4 * (u & 1) + ((u >> 1) & 3)
+         : CPR == 4  ? (u & 3)
+                     : (u & 1);
+  }
   static __device__ __forceinline__ int off(int row, int chunk) {
     return row * (2 * D) + ((chunk ^ swz(row)) << 4);
+  }
+  // The K fragment offsets are reused 32 rows down and the V offsets 16 rows
+  // down: both steps must leave the swizzle unchanged.
+  static constexpr bool steps_keep_swizzle() {
+    for (int r = 0; r < 16; ++r)
+      if (swz(r + 32) != swz(r) || swz(r + 16) != swz(r) || swz(r + 48) != swz(r)) return false;
+    return true;
   }
 };
 
@@ -129,10 +144,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int NB = DP / 32;          // 32-row blocks of O^T
   constexpr int NT = NW * 64;          // threads per workgroup
   constexpr int TILE = BN * D * 2;     // bytes of one K or V tile
-  // Moving 32 rows (K blocks) or 8 rows (V halves) keeps each row's swizzle,
-  // so those steps are plain constant offsets.
-  static_assert((2 * 32 / G::RPL) % G::CPR == 0, "K block step must keep the swizzle");
-  static_assert((2 * 8 / G::RPL) % G::CPR == 0, "V row step must keep the swizzle");
+  static_assert(G::steps_keep_swizzle(), "tile steps must keep the LDS swizzle");
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][TILE];  // [buf][K, V]
 
@@ -190,15 +202,20 @@ void prefill_mfma_kernel(PrefillArgs a) {
   int koff[KC];  // K fragment of k-chunk kc for key l32 (+32 rows for block 1)
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) koff[kc] = G::off(l32, 2 * kc + h32);
-  int voff[NB];  // transpose-read address: key 4*h32 + i/4, features 4*(i%4).. of block n
+  // Transpose-read addresses: key 8*half + 4*h32 + i/4 (+16 per key group),
+  // features 4*(i%4).. of feature block n, with i = lane % 16.
+  int voff[NB][2];
   {
     const int i = lane & 15;
-    const int row = 4 * h32 + (i >> 2);
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      int col = 16 * ((lane >> 4) & 1) + 32 * n + 4 * (i & 3);
-      if (col >= D) col -= D;  // D = 16: O^T rows 16..31 are computed, then discarded
-      voff[n] = G::off(row, col >> 3) + ((col & 7) << 1);
+    for (int half = 0; half < 2; ++half) {
+      const int row = 8 * half + 4 * h32 + (i >> 2);
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        int col = 16 * ((lane >> 4) & 1) + 32 * n + 4 * (i & 3);
+        if (col >= D) col -= D;  // D = 16: O^T rows 16..31 are computed, then discarded
+        voff[n][half] = G::off(row, col >> 3) + ((col & 7) << 1);
+      }
     }
   }
 
@@ -321,9 +338,9 @@ void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
       for (int c2 = 0; c2 < BN / 16; ++c2) {
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            LDS_PTR(s16x4, vt + voff[n] + (16 * c2) * 2 * D));
+            LDS_PTR(s16x4, vt + voff[n][0] + 16 * c2 * 2 * D));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            LDS_PTR(s16x4, vt + voff[n] + (16 * c2 + 8) * 2 * D));
+            LDS_PTR(s16x4, vt + voff[n][1] + 16 * c2 * 2 * D));
         vf[n][c2] =
             __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
@@ -410,7 +427,11 @@ hipError_t launch_typed(const Problem& p) {
   return hipGetLastError();
 }
 
-constexpr int kWaves = 8;
+// Waves per workgroup (32 query rows each); a build-time tuning knob.
+#ifndef ATTN_PREFILL_WAVES
+#define ATTN_PREFILL_WAVES 8
+#endif
+constexpr int kWaves = ATTN_PREFILL_WAVES;
 
 template <typename T, int D>
 hipError_t launch_d(const Problem& p) {

@@ -98,6 +98,15 @@ struct PrefillArgs {
 };
 
 constexpr int kBN = 64;              // keys per tile
+// LDS operand reads in flight ahead of the MFMA that uses them.
+#ifndef ATTN_KPF
+#define ATTN_KPF 6
+#endif
+#ifndef ATTN_VPF
+#define ATTN_VPF 4
+#endif
+constexpr int kKPF = ATTN_KPF;
+constexpr int kVPF = ATTN_VPF;
 constexpr float kRefreshGap = 8.0f;  // base-2 units; see the file comment
 
 // Tile geometry: rows of D halves (2*D bytes) in 16-byte chunks, chunk c of
@@ -127,8 +136,17 @@ template <int D> struct Geo {
   }
 };
 
-// x from lane l ^ 32 (the other half-wave).
-__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32); }
+// max / sum of x over lanes l and l ^ 32 (the two half-waves), on the VALU
+// (no LDS round trip): v_permlane32_swap leaves {x[l], x[l ^ 32]} in its two
+// results.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <typename T, int D, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
@@ -265,21 +283,47 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const unsigned char* kt = &smem[buf][0][0];
     const unsigned char* vt = &smem[buf][1][0];
 
-    // S^T = K Q^T for two 32-key blocks; every K fragment of the tile is
-    // requested before the first MFMA so LDS latency overlaps the math.
-    vec8 kf[BN / 32][KC];
+    // S^T = K Q^T.  MFMA i uses K fragment i (key block i / KC, feature
+    // chunk i % KC); each fragment is read KPF MFMAs ahead so LDS latency
+    // hides behind the matrix work, and scheduling barriers keep that order.
+    constexpr int NS = (BN / 32) * KC;
+    vec8 kf[NS];
+    auto kread = [&](int i) {
+      return *reinterpret_cast<const vec8*>(kt + koff[i % KC] + (i / KC) * 32 * 2 * D);
+    };
 #pragma unroll
-    for (int mb = 0; mb < BN / 32; ++mb)
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        kf[mb][kc] = *reinterpret_cast<const vec8*>(kt + koff[kc] + mb * 32 * 2 * D);
+    for (int i = 0; i < kKPF && i < NS; ++i) kf[i] = kread(i);
     f32x16 s[BN / 32];
 #pragma unroll
-    for (int mb = 0; mb < BN / 32; ++mb) {
-      s[mb] = f32x16{};
+    for (int mb = 0; mb < BN / 32; ++mb) s[mb] = f32x16{};
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) s[mb] = Mfma<T>::mma(kf[mb][kc], qf[kc], s[mb]);
+    for (int i = 0; i < NS; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + kKPF < NS) kf[i + kKPF] = kread(i + kKPF);
+      s[i / KC] = Mfma<T>::mma(kf[i], qf[i % KC], s[i / KC]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // The first V^T operands of O^T += V^T P^T do not depend on the softmax:
+    // request them now so they arrive while it runs.  Slot e (0..3) of the
+    // first transpose read is key 16*c2 + 4*h32 + e, of the second key
+    // 16*c2 + 8 + 4*h32 + e: the keys that registers 8*(c2&1) + 0..7 of S^T
+    // block c2/2 hold.  Operand i is feature block i / (BN/16), key group
+    // i % (BN/16).
+    constexpr int NV = NB * (BN / 16);
+    vec8 vf[NV];
+    auto vread = [&](int i) {
+      const int n = i / (BN / 16), c2 = i % (BN / 16);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          LDS_PTR(s16x4, vt + voff[n][0] + 16 * c2 * 2 * D));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          LDS_PTR(s16x4, vt + voff[n][1] + 16 * c2 * 2 * D));
+      return __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+#pragma unroll
+    for (int i = 0; i < kVPF && i < NV; ++i) vf[i] = vread(i);
+    __builtin_amdgcn_sched_barrier(0);
+
     if (need_mask) {
 #pragma unroll
       for (int mb = 0; mb < BN / 32; ++mb) {
@@ -297,7 +341,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     for (int mb = 0; mb < BN / 32; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-    mx = fmaxf(mx, other_half(mx));
+    mx = half_max(mx);
     const float m_tile = mx * c;  // -inf when nothing in the tile is visible
     m_true = fmaxf(m_true, m_tile);
     const bool refresh = m_tile > m_run + kRefreshGap;
@@ -329,26 +373,15 @@ void prefill_mfma_kernel(PrefillArgs a) {
     }
     l_run += rs;
 
-    // O^T += V^T P^T.  Slot e (0..3) of the first transpose read is key
-    // 16*c2 + 4*h32 + e, of the second key 16*c2 + 8 + 4*h32 + e: the keys
-    // that registers 8*(c2&1) + 0..7 of S^T block c2/2 hold.
-    vec8 vf[NB][BN / 16];
+    // O^T += V^T P^T, each V^T operand read kVPF MFMAs ahead.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
-#pragma unroll
-      for (int c2 = 0; c2 < BN / 16; ++c2) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            LDS_PTR(s16x4, vt + voff[n][0] + 16 * c2 * 2 * D));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            LDS_PTR(s16x4, vt + voff[n][1] + 16 * c2 * 2 * D));
-        vf[n][c2] =
-            __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
+    for (int i = 0; i < NV; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + kVPF < NV) vf[i + kVPF] = vread(i + kVPF);
+      acc[i / (BN / 16)] = Mfma<T>::mma(vf[i], pf[i % (BN / 16)], acc[i / (BN / 16)]);
     }
-#pragma unroll
-    for (int n = 0; n < NB; ++n)
-#pragma unroll
-      for (int c2 = 0; c2 < BN / 16; ++c2) acc[n] = Mfma<T>::mma(vf[n][c2], pf[c2], acc[n]);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   if (ntiles > 0) {
@@ -377,7 +410,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
   }
 
   // Epilogue: join the two half-wave sums, normalise, one cast, store.
-  const float l_tot = l_run + other_half(l_run);
+  const float l_tot = half_sum(l_run);
   if (qrow < Nq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     T* orow = Oh + (int64_t)qrow * D;

@@ -92,7 +92,8 @@ struct PrefillArgs {
   float* l_out;
   int Nq, Nk;
   int nqt;      // query tiles per (b, h)
-  int total;    // (B*H) * nqt real workgroups
+  int nwork;    // workgroups per (b, h): nqt, or ceil(nqt / 2) paired causal tiles
+  int total;    // (B*H) * nwork real workgroups
   int per_xcd;  // gridDim.x / 8
   float c;      // scale * log2(e)
 };
@@ -166,275 +167,281 @@ void prefill_mfma_kernel(PrefillArgs a) {
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][TILE];  // [buf][K, V]
 
-  // Workgroup -> (head, query tile).  Consecutive workgroup ids land on
+  // Workgroup -> (head, query tiles).  Consecutive workgroup ids land on
   // different XCDs (round-robin over 8); regroup them so each XCD walks a
-  // contiguous range of heads and their K/V stays in that XCD's L2.  Within
-  // a head, causal tiles go longest-first.
+  // contiguous range of heads and their K/V stays in that XCD's L2.
+  // Causal: a workgroup takes query tile nqt-1-r and then tile r of its
+  // head, so every workgroup streams the same number of key tiles and the
+  // grid fills the CUs evenly (with one tile per workgroup, the short
+  // diagonal tiles at the end of each XCD's range leave CUs idle).
   const int bid = blockIdx.x;
   const int logical = (bid & 7) * a.per_xcd + (bid >> 3);
   if (logical >= a.total) return;
-  const int bh = logical / a.nqt;
-  const int rr = logical - bh * a.nqt;
-  const int qt = CAUSAL ? (a.nqt - 1 - rr) : rr;
+  const int bh = logical / a.nwork;
+  const int rr = logical - bh * a.nwork;
+  const int npass = CAUSAL && a.nqt - 1 - rr != rr ? 2 : 1;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int qt = CAUSAL ? (pass == 0 ? a.nqt - 1 - rr : rr) : rr;
 
-  const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
-  const T* __restrict__ Qh = static_cast<const T*>(a.q) + (int64_t)bh * Nq * D;
-  const T* Kh = static_cast<const T*>(a.k) + (int64_t)bh * Nk * D;
-  const T* Vh = static_cast<const T*>(a.v) + (int64_t)bh * Nk * D;
-  T* __restrict__ Oh = static_cast<T*>(a.o) + (int64_t)bh * Nq * D;
+    const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
+    const T* __restrict__ Qh = static_cast<const T*>(a.q) + (int64_t)bh * Nq * D;
+    const T* Kh = static_cast<const T*>(a.k) + (int64_t)bh * Nk * D;
+    const T* Vh = static_cast<const T*>(a.v) + (int64_t)bh * Nk * D;
+    T* __restrict__ Oh = static_cast<T*>(a.o) + (int64_t)bh * Nq * D;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h32 = lane >> 5;
-  const int l32 = lane & 31;
-  const int i0 = qt * BM;
-  const int qw0 = i0 + wave * 32;  // first query row of this wave
-  const int qrow = qw0 + l32;      // this lane's query row
-  const float c = a.c;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h32 = lane >> 5;
+    const int l32 = lane & 31;
+    const int i0 = qt * BM;
+    const int qw0 = i0 + wave * 32;  // first query row of this wave
+    const int qrow = qw0 + l32;      // this lane's query row
+    const float c = a.c;
 
-  // Q fragment: B operand, 8 consecutive features per k-chunk.  Rows past
-  // Nq (ghost rows) are zero so their scores stay finite; never stored.
-  vec8 qf[KC];
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    qf[kc] = qrow < Nq
-                 ? *reinterpret_cast<const vec8*>(Qh + (int64_t)qrow * D + kc * 16 + h32 * 8)
-                 : vec8{};
-  }
-
-  // Key range that holds a visible key for some real row of this tile.
-  int kend = Nk;
-  if (CAUSAL) kend = min(Nk, min(i0 + BM, Nq) + off);
-  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
-
-  // Buffer resources over this head's K and V: offsets at or past Nk rows
-  // are out of range and read as zero.
-  const uint32_t kv_bytes = (uint32_t)Nk * (uint32_t)(2 * D);
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(Kh), 0, (int)kv_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(Vh), 0, (int)kv_bytes, 0x00020000);
-
-  // Per-lane LDS byte offsets, loop invariant.
-  int koff[KC];  // K fragment of k-chunk kc for key l32 (+32 rows for block 1)
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) koff[kc] = G::off(l32, 2 * kc + h32);
-  // Transpose-read addresses: key 8*half + 4*h32 + i/4 (+16 per key group),
-  // features 4*(i%4).. of feature block n, with i = lane % 16.
-  int voff[NB][2];
-  {
-    const int i = lane & 15;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int row = 8 * half + 4 * h32 + (i >> 2);
-#pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        int col = 16 * ((lane >> 4) & 1) + 32 * n + 4 * (i & 3);
-        if (col >= D) col -= D;  // D = 16: O^T rows 16..31 are computed, then discarded
-        voff[n][half] = G::off(row, col >> 3) + ((col & 7) << 1);
-      }
+    // Q fragment: B operand, 8 consecutive features per k-chunk.  Rows past
+    // Nq (ghost rows) are zero so their scores stay finite; never stored.
+    vec8 qf[KC];
+  #pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      qf[kc] = qrow < Nq
+                   ? *reinterpret_cast<const vec8*>(Qh + (int64_t)qrow * D + kc * 16 + h32 * 8)
+                   : vec8{};
     }
-  }
 
-  float m_run = kNegInf;   // reference max for the exponentials, base-2 units
-  float m_true = kNegInf;  // exact running max, base-2 units
-  float l_run = 0.f;       // this half-wave's share of the running sum
-  f32x16 acc[NB];
-#pragma unroll
-  for (int n = 0; n < NB; ++n) acc[n] = f32x16{};
+    // Key range that holds a visible key for some real row of this tile.
+    int kend = Nk;
+    if (CAUSAL) kend = min(Nk, min(i0 + BM, Nq) + off);
+    const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
 
-  // Tile staging: each thread moves NPT 16-byte slots of K and of V per tile,
-  // HBM -> registers (buffer loads: rows past Nk are out of range and read
-  // as zero) -> LDS.  LDS slot s holds chunk (s % CPR) ^ swz(row) of row
-  // s / CPR, so consecutive lanes write consecutive 16 bytes and read a
-  // permutation of one row's chunks (still one coalesced row per 16 lanes
-  // for D = 128).
-  constexpr int NSLOT = TILE / 16;
-  constexpr int NPT = (NSLOT + NT - 1) / NT;
-  u32x4 kreg[NPT], vreg[NPT];
-  auto load_tile = [&](int j0) {
-#pragma unroll
-    for (int u = 0; u < NPT; ++u) {
-      const int sl = tid + u * NT;
-      if (NSLOT % NT == 0 || sl < NSLOT) {
-        const int row = sl / G::CPR;
-        const int chunk = (sl % G::CPR) ^ G::swz(row);
-        const int j = min(j0 + row, Nk);  // rows past Nk: out of range, read as 0
-        const uint32_t vo = (uint32_t)j * (uint32_t)(2 * D) + (uint32_t)(chunk << 4);
-        kreg[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)vo, 0, 0);
-        vreg[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)vo, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < NPT; ++u) {
-      const int sl = tid + u * NT;
-      if (NSLOT % NT == 0 || sl < NSLOT) {
-        *reinterpret_cast<u32x4*>(&smem[buf][0][sl * 16]) = kreg[u];
-        *reinterpret_cast<u32x4*>(&smem[buf][1][sl * 16]) = vreg[u];
-      }
-    }
-  };
+    // Buffer resources over this head's K and V: offsets at or past Nk rows
+    // are out of range and read as zero.
+    const uint32_t kv_bytes = (uint32_t)Nk * (uint32_t)(2 * D);
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(Kh), 0, (int)kv_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(Vh), 0, (int)kv_bytes, 0x00020000);
 
-  auto compute = [&](auto bufc, int j0, bool need_mask) {
-    constexpr int buf = decltype(bufc)::value;
-    const unsigned char* kt = &smem[buf][0][0];
-    const unsigned char* vt = &smem[buf][1][0];
-
-    // S^T = K Q^T.  MFMA i uses K fragment i (key block i / KC, feature
-    // chunk i % KC); each fragment is read KPF MFMAs ahead so LDS latency
-    // hides behind the matrix work, and scheduling barriers keep that order.
-    constexpr int NS = (BN / 32) * KC;
-    vec8 kf[NS];
-    auto kread = [&](int i) {
-      return *reinterpret_cast<const vec8*>(kt + koff[i % KC] + (i / KC) * 32 * 2 * D);
-    };
-#pragma unroll
-    for (int i = 0; i < kKPF && i < NS; ++i) kf[i] = kread(i);
-    f32x16 s[BN / 32];
-#pragma unroll
-    for (int mb = 0; mb < BN / 32; ++mb) s[mb] = f32x16{};
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (i + kKPF < NS) kf[i + kKPF] = kread(i + kKPF);
-      s[i / KC] = Mfma<T>::mma(kf[i], qf[i % KC], s[i / KC]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // The first V^T operands of O^T += V^T P^T do not depend on the softmax:
-    // request them now so they arrive while it runs.  Slot e (0..3) of the
-    // first transpose read is key 16*c2 + 4*h32 + e, of the second key
-    // 16*c2 + 8 + 4*h32 + e: the keys that registers 8*(c2&1) + 0..7 of S^T
-    // block c2/2 hold.  Operand i is feature block i / (BN/16), key group
-    // i % (BN/16).
-    constexpr int NV = NB * (BN / 16);
-    vec8 vf[NV];
-    auto vread = [&](int i) {
-      const int n = i / (BN / 16), c2 = i % (BN / 16);
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          LDS_PTR(s16x4, vt + voff[n][0] + 16 * c2 * 2 * D));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          LDS_PTR(s16x4, vt + voff[n][1] + 16 * c2 * 2 * D));
-      return __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-#pragma unroll
-    for (int i = 0; i < kVPF && i < NV; ++i) vf[i] = vread(i);
-    __builtin_amdgcn_sched_barrier(0);
-
-    if (need_mask) {
-#pragma unroll
-      for (int mb = 0; mb < BN / 32; ++mb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + mb * 32 + (r >> 2) * 8 + h32 * 4 + (r & 3);
-          const bool vis = j < Nk && (!CAUSAL || j <= qrow + off);
-          s[mb][r] = vis ? s[mb][r] : kNegInf;
+    // Per-lane LDS byte offsets, loop invariant.
+    int koff[KC];  // K fragment of k-chunk kc for key l32 (+32 rows for block 1)
+  #pragma unroll
+    for (int kc = 0; kc < KC; ++kc) koff[kc] = G::off(l32, 2 * kc + h32);
+    // Transpose-read addresses: key 8*half + 4*h32 + i/4 (+16 per key group),
+    // features 4*(i%4).. of feature block n, with i = lane % 16.
+    int voff[NB][2];
+    {
+      const int i = lane & 15;
+  #pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int row = 8 * half + 4 * h32 + (i >> 2);
+  #pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          int col = 16 * ((lane >> 4) & 1) + 32 * n + 4 * (i & 3);
+          if (col >= D) col -= D;  // D = 16: O^T rows 16..31 are computed, then discarded
+          voff[n][half] = G::off(row, col >> 3) + ((col & 7) << 1);
         }
       }
     }
-    // Tile max of this row: in-lane, then across the two half-waves.
-    float mx = s[0][0];
-#pragma unroll
-    for (int mb = 0; mb < BN / 32; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-    mx = half_max(mx);
-    const float m_tile = mx * c;  // -inf when nothing in the tile is visible
-    m_true = fmaxf(m_true, m_tile);
-    const bool refresh = m_tile > m_run + kRefreshGap;
-    if (__builtin_amdgcn_ballot_w64(refresh)) {
-      const float m_new = refresh ? m_tile : m_run;
-      const float alpha = exp2_hw(m_run - pinned_ref(m_new));
-      l_run *= alpha;
-#pragma unroll
-      for (int n = 0; n < NB; ++n) acc[n] *= alpha;
-      m_run = m_new;
-    }
-    const float ref = pinned_ref(m_run);
-#pragma unroll
-    for (int mb = 0; mb < BN / 32; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[mb][r] = exp2_hw(__builtin_fmaf(s[mb][r], c, -ref));
 
-    // P^T rounded to the input type: the B operand of O^T += V^T P^T.  The
-    // row sum adds the same rounded weights, so the normalisation matches
-    // the numerator exactly (one visible key gives weight 1 and out = V).
-    vec8 pf[BN / 16];
-    float rs = 0.f;
-#pragma unroll
-    for (int c2 = 0; c2 < BN / 16; ++c2) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[c2][e] = from_f32<T>(s[c2 >> 1][(c2 & 1) * 8 + e]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rs = Mfma<T>::sum2(vec2{pf[c2][2 * e], pf[c2][2 * e + 1]}, rs);
-    }
-    l_run += rs;
+    float m_run = kNegInf;   // reference max for the exponentials, base-2 units
+    float m_true = kNegInf;  // exact running max, base-2 units
+    float l_run = 0.f;       // this half-wave's share of the running sum
+    f32x16 acc[NB];
+  #pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] = f32x16{};
 
-    // O^T += V^T P^T, each V^T operand read kVPF MFMAs ahead.
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (i + kVPF < NV) vf[i + kVPF] = vread(i + kVPF);
-      acc[i / (BN / 16)] = Mfma<T>::mma(vf[i], pf[i % (BN / 16)], acc[i / (BN / 16)]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
+    // Tile staging: each thread moves NPT 16-byte slots of K and of V per tile,
+    // HBM -> registers (buffer loads: rows past Nk are out of range and read
+    // as zero) -> LDS.  LDS slot s holds chunk (s % CPR) ^ swz(row) of row
+    // s / CPR, so consecutive lanes write consecutive 16 bytes and read a
+    // permutation of one row's chunks (still one coalesced row per 16 lanes
+    // for D = 128).
+    constexpr int NSLOT = TILE / 16;
+    constexpr int NPT = (NSLOT + NT - 1) / NT;
+    u32x4 kreg[NPT], vreg[NPT];
+    auto load_tile = [&](int j0) {
+  #pragma unroll
+      for (int u = 0; u < NPT; ++u) {
+        const int sl = tid + u * NT;
+        if (NSLOT % NT == 0 || sl < NSLOT) {
+          const int row = sl / G::CPR;
+          const int chunk = (sl % G::CPR) ^ G::swz(row);
+          const int j = min(j0 + row, Nk);  // rows past Nk: out of range, read as 0
+          const uint32_t vo = (uint32_t)j * (uint32_t)(2 * D) + (uint32_t)(chunk << 4);
+          kreg[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)vo, 0, 0);
+          vreg[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)vo, 0, 0);
+        }
+      }
+    };
+    auto store_tile = [&](int buf) {
+  #pragma unroll
+      for (int u = 0; u < NPT; ++u) {
+        const int sl = tid + u * NT;
+        if (NSLOT % NT == 0 || sl < NSLOT) {
+          *reinterpret_cast<u32x4*>(&smem[buf][0][sl * 16]) = kreg[u];
+          *reinterpret_cast<u32x4*>(&smem[buf][1][sl * 16]) = vreg[u];
+        }
+      }
+    };
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    const int q_last = min(qw0 + 32, Nq) - 1;  // last real row of this wave
-    auto step = [&](auto bufc, int t) {
+    auto compute = [&](auto bufc, int j0, bool need_mask) {
       constexpr int buf = decltype(bufc)::value;
-      const int j0 = t * BN;
-      const bool more = t + 1 < ntiles;
-      if (more) load_tile(j0 + BN);  // in flight while this tile is computed
-      const bool active = qw0 < Nq && (!CAUSAL || j0 <= q_last + off);
-      if (active) {
-        const bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + off);
-        compute(bufc, j0, need_mask);
-      }
-      // Buffer buf^1 was last read in step t-1, before that step's barrier.
-      if (more) store_tile(buf ^ 1);
-      __syncthreads();
-    };
-    for (int t = 0; t < ntiles; t += 2) {
-      step(std::integral_constant<int, 0>{}, t);
-      if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
-    }
-  }
+      const unsigned char* kt = &smem[buf][0][0];
+      const unsigned char* vt = &smem[buf][1][0];
 
-  // Epilogue: join the two half-wave sums, normalise, one cast, store.
-  const float l_tot = half_sum(l_run);
-  if (qrow < Nq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    T* orow = Oh + (int64_t)qrow * D;
-#pragma unroll
-    for (int n = 0; n < NB; ++n) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = n * 32 + g * 8 + h32 * 4;
-        if (d0 < D) {
-          vec4 o4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o4[e] = from_f32<T>(acc[n][g * 4 + e] * inv);
-          *reinterpret_cast<vec4*>(orow + d0) = o4;
+      // S^T = K Q^T.  MFMA i uses K fragment i (key block i / KC, feature
+      // chunk i % KC); each fragment is read KPF MFMAs ahead so LDS latency
+      // hides behind the matrix work, and scheduling barriers keep that order.
+      constexpr int NS = (BN / 32) * KC;
+      vec8 kf[NS];
+      auto kread = [&](int i) {
+        return *reinterpret_cast<const vec8*>(kt + koff[i % KC] + (i / KC) * 32 * 2 * D);
+      };
+  #pragma unroll
+      for (int i = 0; i < kKPF && i < NS; ++i) kf[i] = kread(i);
+      f32x16 s[BN / 32];
+  #pragma unroll
+      for (int mb = 0; mb < BN / 32; ++mb) s[mb] = f32x16{};
+  #pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + kKPF < NS) kf[i + kKPF] = kread(i + kKPF);
+        s[i / KC] = Mfma<T>::mma(kf[i], qf[i % KC], s[i / KC]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // The first V^T operands of O^T += V^T P^T do not depend on the softmax:
+      // request them now so they arrive while it runs.  Slot e (0..3) of the
+      // first transpose read is key 16*c2 + 4*h32 + e, of the second key
+      // 16*c2 + 8 + 4*h32 + e: the keys that registers 8*(c2&1) + 0..7 of S^T
+      // block c2/2 hold.  Operand i is feature block i / (BN/16), key group
+      // i % (BN/16).
+      constexpr int NV = NB * (BN / 16);
+      vec8 vf[NV];
+      auto vread = [&](int i) {
+        const int n = i / (BN / 16), c2 = i % (BN / 16);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            LDS_PTR(s16x4, vt + voff[n][0] + 16 * c2 * 2 * D));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            LDS_PTR(s16x4, vt + voff[n][1] + 16 * c2 * 2 * D));
+        return __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+  #pragma unroll
+      for (int i = 0; i < kVPF && i < NV; ++i) vf[i] = vread(i);
+      __builtin_amdgcn_sched_barrier(0);
+
+      if (need_mask) {
+  #pragma unroll
+        for (int mb = 0; mb < BN / 32; ++mb) {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = j0 + mb * 32 + (r >> 2) * 8 + h32 * 4 + (r & 3);
+            const bool vis = j < Nk && (!CAUSAL || j <= qrow + off);
+            s[mb][r] = vis ? s[mb][r] : kNegInf;
+          }
         }
       }
+      // Tile max of this row: in-lane, then across the two half-waves.
+      float mx = s[0][0];
+  #pragma unroll
+      for (int mb = 0; mb < BN / 32; ++mb)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+      mx = half_max(mx);
+      const float m_tile = mx * c;  // -inf when nothing in the tile is visible
+      m_true = fmaxf(m_true, m_tile);
+      const bool refresh = m_tile > m_run + kRefreshGap;
+      if (__builtin_amdgcn_ballot_w64(refresh)) {
+        const float m_new = refresh ? m_tile : m_run;
+        const float alpha = exp2_hw(m_run - pinned_ref(m_new));
+        l_run *= alpha;
+  #pragma unroll
+        for (int n = 0; n < NB; ++n) acc[n] *= alpha;
+        m_run = m_new;
+      }
+      const float ref = pinned_ref(m_run);
+  #pragma unroll
+      for (int mb = 0; mb < BN / 32; ++mb)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) s[mb][r] = exp2_hw(__builtin_fmaf(s[mb][r], c, -ref));
+
+      // P^T rounded to the input type: the B operand of O^T += V^T P^T.  The
+      // row sum adds the same rounded weights, so the normalisation matches
+      // the numerator exactly (one visible key gives weight 1 and out = V).
+      vec8 pf[BN / 16];
+      float rs = 0.f;
+  #pragma unroll
+      for (int c2 = 0; c2 < BN / 16; ++c2) {
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) pf[c2][e] = from_f32<T>(s[c2 >> 1][(c2 & 1) * 8 + e]);
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) rs = Mfma<T>::sum2(vec2{pf[c2][2 * e], pf[c2][2 * e + 1]}, rs);
+      }
+      l_run += rs;
+
+      // O^T += V^T P^T, each V^T operand read kVPF MFMAs ahead.
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + kVPF < NV) vf[i + kVPF] = vread(i + kVPF);
+        acc[i / (BN / 16)] = Mfma<T>::mma(vf[i], pf[i % (BN / 16)], acc[i / (BN / 16)]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    if (ntiles > 0) {
+      load_tile(0);
+      store_tile(0);
+      __syncthreads();
+      const int q_last = min(qw0 + 32, Nq) - 1;  // last real row of this wave
+      auto step = [&](auto bufc, int t) {
+        constexpr int buf = decltype(bufc)::value;
+        const int j0 = t * BN;
+        const bool more = t + 1 < ntiles;
+        if (more) load_tile(j0 + BN);  // in flight while this tile is computed
+        const bool active = qw0 < Nq && (!CAUSAL || j0 <= q_last + off);
+        if (active) {
+          const bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + off);
+          compute(bufc, j0, need_mask);
+        }
+        // Buffer buf^1 was last read in step t-1, before that step's barrier.
+        if (more) store_tile(buf ^ 1);
+        __syncthreads();
+      };
+      for (int t = 0; t < ntiles; t += 2) {
+        step(std::integral_constant<int, 0>{}, t);
+        if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
+      }
     }
-    if (h32 == 0) {
-      // Row state relative to the exact max: sum exp = l * e^m.
-      const int64_t row = (int64_t)bh * Nq + qrow;
-      const float to_true = m_true == kNegInf ? 0.f : exp2_hw(m_run - m_true);
-      if (a.m_out) a.m_out[row] = m_true * kLn2;
-      if (a.l_out) a.l_out[row] = l_tot * to_true;
+
+    // Epilogue: join the two half-wave sums, normalise, one cast, store.
+    const float l_tot = half_sum(l_run);
+    if (qrow < Nq) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      T* orow = Oh + (int64_t)qrow * D;
+  #pragma unroll
+      for (int n = 0; n < NB; ++n) {
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = n * 32 + g * 8 + h32 * 4;
+          if (d0 < D) {
+            vec4 o4;
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) o4[e] = from_f32<T>(acc[n][g * 4 + e] * inv);
+            *reinterpret_cast<vec4*>(orow + d0) = o4;
+          }
+        }
+      }
+      if (h32 == 0) {
+        // Row state relative to the exact max: sum exp = l * e^m.
+        const int64_t row = (int64_t)bh * Nq + qrow;
+        const float to_true = m_true == kNegInf ? 0.f : exp2_hw(m_run - m_true);
+        if (a.m_out) a.m_out[row] = m_true * kLn2;
+        if (a.l_out) a.l_out[row] = l_tot * to_true;
+      }
     }
-  }
+  }  // pass
 }
 
 template <typename T, int D, int NW, bool CAUSAL>
@@ -450,7 +457,8 @@ hipError_t launch_typed(const Problem& p) {
   a.Nq = (int)p.Nq;
   a.Nk = (int)p.Nk;
   a.nqt = (int)((p.Nq + BM - 1) / BM);
-  const int64_t total = p.B * p.H * a.nqt;
+  a.nwork = CAUSAL ? (a.nqt + 1) / 2 : a.nqt;
+  const int64_t total = p.B * p.H * a.nwork;
   a.total = (int)total;
   const int64_t grid = (total + 7) / 8 * 8;
   a.per_xcd = (int)(grid / 8);

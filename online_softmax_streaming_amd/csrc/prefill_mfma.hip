@@ -13,9 +13,10 @@
 //   * Each wave owns 32 query rows.  Its Q rows stay in registers for the
 //     whole kernel as the B operand of v_mfma_f32_32x32x16_{bf16,f16}.
 //   * Key tiles of BN = 64 rows of K and V are staged in LDS, double-buffered:
-//     buffer loads for tile t+1 are in flight while tile t is computed, and
-//     rows past Nk fall outside the buffer's range and arrive as zeros, so
-//     the ragged tail needs no branch.  Both tiles are stored row-major with
+//     buffer loads with the LDS modifier move tile t+1 from HBM straight
+//     into LDS (no register round trip, no LDS store instructions) while
+//     tile t is computed, and rows past Nk fall outside the buffer's range
+//     and arrive as zeros, so the ragged tail needs no branch.  Both tiles are stored row-major with
 //     an XOR swizzle of 16-byte chunks that makes every LDS read below
 //     bank-conflict free.
 //   * S^T = K Q^T is formed per 32-key block, so each lane owns one query
@@ -165,7 +166,13 @@ void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int TILE = BN * D * 2;     // bytes of one K or V tile
   static_assert(G::steps_keep_swizzle(), "tile steps must keep the LDS swizzle");
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][TILE];  // [buf][K, V]
+  // Two LDS buffers as separate objects, so the compiler can tell the
+  // direct-to-LDS loads into one from the operand reads of the other.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem0[2][TILE];  // [K, V]
+  __shared__ __attribute__((aligned(1024))) unsigned char smem1[2][TILE];
+  auto tile_ptr = [&](int buf, int kv) __attribute__((always_inline)) -> unsigned char* {
+    return buf == 0 ? &smem0[kv][0] : &smem1[kv][0];
+  };
 
   // Workgroup -> (head, query tiles).  Consecutive workgroup ids land on
   // different XCDs (round-robin over 8); regroup them so each XCD walks a
@@ -250,44 +257,42 @@ void prefill_mfma_kernel(PrefillArgs a) {
   #pragma unroll
     for (int n = 0; n < NB; ++n) acc[n] = f32x16{};
 
-    // Tile staging: each thread moves NPT 16-byte slots of K and of V per tile,
-    // HBM -> registers (buffer loads: rows past Nk are out of range and read
-    // as zero) -> LDS.  LDS slot s holds chunk (s % CPR) ^ swz(row) of row
-    // s / CPR, so consecutive lanes write consecutive 16 bytes and read a
-    // permutation of one row's chunks (still one coalesced row per 16 lanes
-    // for D = 128).
+    // Tile staging: each thread moves NPT 16-byte slots of K and of V per
+    // tile.  LDS slot s holds chunk (s % CPR) ^ swz(row) of row s / CPR, so
+    // consecutive lanes fill consecutive 16 bytes of LDS and read a
+    // permutation of one row's chunks (one coalesced row per 16 lanes for
+    // D = 128).
     constexpr int NSLOT = TILE / 16;
     constexpr int NPT = (NSLOT + NT - 1) / NT;
-    u32x4 kreg[NPT], vreg[NPT];
-    auto load_tile = [&](int j0) {
+    static_assert(NSLOT % 64 == 0, "a wave moves whole 1 KB LDS blocks");
+    // Tile staging straight from HBM into LDS (buffer loads with the LDS
+    // modifier): lane l of a wave writes the 16 bytes at the wave's block
+    // base + 16*l, i.e. LDS slot s = tid + u*NT, which holds chunk
+    // (s % CPR) ^ swz(row) of row s / CPR.  Rows past Nk are out of the
+    // buffer range and arrive as zeros.  The barrier after the step waits
+    // for these loads (its fence covers writes into LDS by the loads).
+    auto load_tile = [&](int j0, int buf) __attribute__((always_inline)) {
   #pragma unroll
       for (int u = 0; u < NPT; ++u) {
         const int sl = tid + u * NT;
-        if (NSLOT % NT == 0 || sl < NSLOT) {
+        const int sl0 = wave * 64 + u * NT;  // first slot of this wave's block
+        if (NSLOT % NT == 0 || sl0 < NSLOT) {
           const int row = sl / G::CPR;
           const int chunk = (sl % G::CPR) ^ G::swz(row);
           const int j = min(j0 + row, Nk);  // rows past Nk: out of range, read as 0
           const uint32_t vo = (uint32_t)j * (uint32_t)(2 * D) + (uint32_t)(chunk << 4);
-          kreg[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)vo, 0, 0);
-          vreg[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)vo, 0, 0);
-        }
-      }
-    };
-    auto store_tile = [&](int buf) {
-  #pragma unroll
-      for (int u = 0; u < NPT; ++u) {
-        const int sl = tid + u * NT;
-        if (NSLOT % NT == 0 || sl < NSLOT) {
-          *reinterpret_cast<u32x4*>(&smem[buf][0][sl * 16]) = kreg[u];
-          *reinterpret_cast<u32x4*>(&smem[buf][1][sl * 16]) = vreg[u];
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, LDS_PTR(void, tile_ptr(buf, 0) + sl0 * 16),
+                                                   16, (int)vo, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, LDS_PTR(void, tile_ptr(buf, 1) + sl0 * 16),
+                                                   16, (int)vo, 0, 0, 0);
         }
       }
     };
 
     auto compute = [&](auto bufc, int j0, bool need_mask) {
       constexpr int buf = decltype(bufc)::value;
-      const unsigned char* kt = &smem[buf][0][0];
-      const unsigned char* vt = &smem[buf][1][0];
+      const unsigned char* kt = tile_ptr(buf, 0);
+      const unsigned char* vt = tile_ptr(buf, 1);
 
       // S^T = K Q^T.  MFMA i uses K fragment i (key block i / KC, feature
       // chunk i % KC); each fragment is read KPF MFMAs ahead so LDS latency
@@ -391,22 +396,20 @@ void prefill_mfma_kernel(PrefillArgs a) {
     };
 
     if (ntiles > 0) {
-      load_tile(0);
-      store_tile(0);
+      load_tile(0, 0);
       __syncthreads();
       const int q_last = min(qw0 + 32, Nq) - 1;  // last real row of this wave
       auto step = [&](auto bufc, int t) {
         constexpr int buf = decltype(bufc)::value;
         const int j0 = t * BN;
         const bool more = t + 1 < ntiles;
-        if (more) load_tile(j0 + BN);  // in flight while this tile is computed
+        if (more) load_tile(j0 + BN, buf ^ 1);  // in flight while this tile is computed
         const bool active = qw0 < Nq && (!CAUSAL || j0 <= q_last + off);
         if (active) {
           const bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + off);
           compute(bufc, j0, need_mask);
         }
         // Buffer buf^1 was last read in step t-1, before that step's barrier.
-        if (more) store_tile(buf ^ 1);
         __syncthreads();
       };
       for (int t = 0; t < ntiles; t += 2) {

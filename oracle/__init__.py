@@ -1,4 +1,4 @@
-"""FP64 CPU oracle for streaming (online-softmax) attention.
+"""FP64 CPU oracle for streaming (online-softmax) attention and row softmax.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 load anything from this package: only ``tests/``, ``__graft_entry__.smoke()``
@@ -8,16 +8,18 @@ constants or helpers with the HIP library under
 
 Sources (three web pages on one subject):
   * "Intermediate and advanced kernel workshops" (the workshops page):
-    section "Scope and contracts" -- the streaming_attention contract.
+    section "Scope and contracts" -- the streaming_attention and
+    split_softmax contracts.
   * "Compare reasoning after your own attempt" (the answer-key page):
-    the A1 / A3 rows of its table, "Worked answers worth memorizing by
-    derivation" (A1 merge, A3 six/seven example) and the closing note that the
-    attention oracle materialises FP64 scores.
+    the A1 / A2 / A3 rows of its table, "Worked answers worth memorizing by
+    derivation" (A1 merge, A2 scratch size, A3 six/seven example) and the
+    closing note that the attention oracle materialises FP64 scores.
   * "Kernel Notes & Checklist": section 4, "The gotchas ledger" (-inf padding
     before a max, 0 before a sum, ghost rows pinned so they cannot give NaN).
 
-Every function here is pinned by ``tests/test_oracle_pins.py`` against values
-the pages print, closed forms, invariants and 50-digit brute force.
+Every function here is pinned by ``tests/test_oracle_pins.py`` and
+``tests/test_softmax_oracle_pins.py`` against values the pages print, closed
+forms, invariants, library routines and 50-digit brute force.
 """
 
 from .attention import (  # noqa: F401
@@ -28,4 +30,10 @@ from .attention import (  # noqa: F401
     online_merge,
     streaming_model,
     visible_mask,
+)
+from .softmax import (  # noqa: F401
+    num_chunks,
+    scratch_bytes,
+    softmax_rows,
+    split_softmax_model,
 )

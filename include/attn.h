@@ -22,7 +22,7 @@
  *     *values* are never scanned: non-finite inputs are outside the contract
  *     ([W], "Scope and contracts": wrappers validate metadata only).
  *   - Status codes: ATTN_OK, ATTN_E_INVALID (bad argument), ATTN_E_UNSUPPORTED
- *     (valid but not built: head size), ATTN_E_HIP (a HIP runtime call or
+ *     (valid but not built: head size, grid limits), ATTN_E_HIP (a HIP runtime call or
  *     kernel launch failed; the HIP error text is in attn_last_error()).
  */
 #ifndef ONLINE_SOFTMAX_STREAMING_ATTN_H
@@ -142,6 +142,46 @@ ATTN_API int online_merge(double m1, double l1, double m2, double l2,
 ATTN_API int online_merge_batch(const float* m1, const float* l1,
                        const float* m2, const float* l2,
                        float* m, float* l, int64_t n, void* stream);
+
+/*
+ * softmax_rows -- row softmax of a wide matrix by the split method
+ * ([W] "Scope and contracts", split_softmax row; [AK] table row A2 and its
+ * worked answer).
+ *
+ * y[i, :] = exp(x[i, :] - max x[i, :]) / sum_j exp(x[i, j] - max x[i, :])
+ * for i < M, computed as three kernels queued on `stream`: per chunk of
+ * `chunk` columns a partial (m, l); per row the A1 merge of the
+ * ceil(N / chunk) partials; then a re-read of x that writes exp(x - m) / l
+ * with one cast to the output type.
+ *
+ * x, y: device pointers to contiguous row-major [M, N] arrays of `dtype`
+ *       (ATTN_F32 / ATTN_F16 / ATTN_BF16), aligned to the element size;
+ *       16-byte aligned rows (x, y 16-byte aligned and N * element size a
+ *       multiple of 16) take vector loads.  y may equal x (in place) but
+ *       must not otherwise overlap it.  Caller-owned; the library allocates
+ *       only the scratch below.
+ * M >= 0 (M == 0 is a no-op), N >= 1 (the pages' contract stops at 131072
+ *       columns; larger N is accepted), M * ceil(N / chunk) < 2^31.
+ * chunk: 256, 512, 1024, 2048 or 4096 columns per chunk, or 0 to let the
+ *       library choose (the largest that still gives 2048 chunks in all).
+ * Values are not scanned: non-finite inputs are outside the contract.
+ * Scratch: FP32 (m, l) per chunk and per row, 8 * M * (T + 1) bytes with
+ *       T = ceil(N / chunk), taken with hipMallocAsync and released with
+ *       hipFreeAsync on `stream`.
+ * Returns ATTN_OK once queued; ATTN_E_INVALID for bad arguments,
+ * ATTN_E_UNSUPPORTED when M * T reaches 2^31, ATTN_E_HIP if a launch or
+ * the scratch allocation fails.
+ */
+ATTN_API int softmax_rows(const void* x, void* y, int64_t M, int64_t N, int64_t chunk,
+                          int dtype, void* stream);
+
+/*
+ * softmax_rows_scratch_bytes -- bytes of scratch softmax_rows takes for
+ * these sizes ([AK] worked answer A2: 1088 for M = 4, N = 32769,
+ * chunk = 1024), or -1 if M < 0, N < 1 or chunk is not accepted.  Host
+ * only; no device work.
+ */
+ATTN_API int64_t softmax_rows_scratch_bytes(int64_t M, int64_t N, int64_t chunk);
 
 /* Static text for a status code; never NULL. */
 ATTN_API const char* attn_strerror(int code);

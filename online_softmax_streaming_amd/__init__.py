@@ -1,4 +1,5 @@
-"""Streaming (online-softmax) attention forward for AMD MI355X (gfx950).
+"""Streaming (online-softmax) attention forward and wide-row split softmax
+for AMD MI355X (gfx950).
 
 The computation lives in the HIP library libattn.so (C ABI in
 include/attn.h); this package is its Python binding plus the seeded
@@ -21,4 +22,6 @@ from .attn import (  # noqa: F401
     default_scale,
     online_merge,
     online_merge_batch,
+    softmax_rows,
+    softmax_rows_scratch_bytes,
 )

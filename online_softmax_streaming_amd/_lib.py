@@ -30,6 +30,8 @@ SIGNATURES = {
                                     ctypes.POINTER(ctypes.c_double)]),
     "online_merge_batch": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64,
                                           _c_ptr]),
+    "softmax_rows": (ctypes.c_int, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_ptr]),
+    "softmax_rows_scratch_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64]),
     "attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_last_error": (ctypes.c_char_p, []),
 }

@@ -159,3 +159,34 @@ def online_merge_batch(m1, l1, m2, l2, m=None, l=None, stream=None):
                                       m1.numel(), sh)
     _check(rc, "online_merge_batch")
     return m, l
+
+
+def softmax_rows(x, chunk=0, out=None, stream=None):
+    """Row softmax of a contiguous 2D GPU tensor by the split method.
+
+    Three kernels on the stream (per-chunk partial states, their A1 merge per
+    row, a normalising re-read); `chunk` is 256/512/1024/2048/4096 columns or
+    0 for the library's choice.  `out` may be `x` itself (in place).
+    """
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError("x must be a GPU tensor; there is no CPU path")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2D tensor [M, N]")
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    if out is None:
+        out = torch.empty_like(x)
+    elif (out.shape != x.shape or out.dtype != x.dtype or out.device != x.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor like x")
+    with torch.cuda.device(x.device):
+        sh = _stream_handle(stream, x.device)
+        rc = lib().softmax_rows(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                x.shape[0], x.shape[1], int(chunk), _DTYPES[x.dtype], sh)
+    _check(rc, "softmax_rows")
+    return out
+
+
+def softmax_rows_scratch_bytes(m, n, chunk=0):
+    """Scratch bytes softmax_rows takes for [m, n] (-1 for invalid sizes)."""
+    return int(lib().softmax_rows_scratch_bytes(int(m), int(n), int(chunk)))

@@ -134,6 +134,20 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
   return e == hipSuccess ? ATTN_OK : hip_fail(e, "prefill kernel launch");
 }
 
+// Chunk size for softmax_rows: the caller's, or (chunk == 0) the largest of
+// 4096, 2048, ..., 256 that still gives >= 2048 workgroups per pass, so
+// narrow matrices with few rows still spread over the CUs.
+int64_t pick_chunk(int64_t M, int64_t N, int64_t chunk) {
+  if (chunk != 0) return chunk;
+  int64_t c = 4096;
+  while (c > 256 && M * attn::softmax_chunks(N, c) < 2048) c /= 2;
+  return c;
+}
+
+bool valid_chunk(int64_t c) {
+  return c == 0 || c == 256 || c == 512 || c == 1024 || c == 2048 || c == 4096;
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,6 +195,46 @@ int online_merge_batch(const float* m1, const float* l1, const float* m2, const 
   const hipError_t e =
       attn::launch_merge_batch(m1, l1, m2, l2, m, l, n, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : hip_fail(e, "merge kernel launch");
+}
+
+int64_t softmax_rows_scratch_bytes(int64_t M, int64_t N, int64_t chunk) {
+  if (M < 0 || N < 1 || !valid_chunk(chunk)) return -1;
+  return attn::softmax_scratch_bytes(M, N, pick_chunk(M, N, chunk));
+}
+
+int softmax_rows(const void* x, void* y, int64_t M, int64_t N, int64_t chunk, int dtype,
+                 void* stream) {
+  g_last_error[0] = '\0';
+  if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_E_INVALID, "dtype %d is not ATTN_F32, ATTN_F16 or ATTN_BF16", dtype);
+  if (M < 0) return fail(ATTN_E_INVALID, "softmax_rows: M < 0");
+  if (N < 1) return fail(ATTN_E_INVALID, "softmax_rows: N must be >= 1, got %lld", (long long)N);
+  if (!valid_chunk(chunk))
+    return fail(ATTN_E_INVALID, "softmax_rows: chunk must be 0, 256, 512, 1024, 2048 or 4096");
+  if (M == 0) return ATTN_OK;
+  if (!x || !y) return fail(ATTN_E_INVALID, "softmax_rows: x and y must be non-NULL");
+  const int64_t elem = dtype == ATTN_F32 ? 4 : 2;
+  if (!aligned(x, elem) || !aligned(y, elem))
+    return fail(ATTN_E_INVALID, "softmax_rows: x and y must be aligned to their element size");
+  if (N > INT64_MAX / elem / M) return fail(ATTN_E_INVALID, "softmax_rows: M*N overflows");
+  const int64_t bytes = M * N * elem;
+  if (x != y && overlaps(x, bytes, y, bytes))
+    return fail(ATTN_E_INVALID, "softmax_rows: y overlaps x without being equal to it");
+  const int64_t c = pick_chunk(M, N, chunk);
+  const int64_t T = attn::softmax_chunks(N, c);
+  if (M > kI32Max || T > kI32Max / M)
+    return fail(ATTN_E_UNSUPPORTED, "softmax_rows: M * ceil(N / chunk) must be < 2^31");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  keep_pool_memory();
+  void* scratch = nullptr;
+  hipError_t e = hipMallocAsync(&scratch, (size_t)attn::softmax_scratch_bytes(M, N, c), s);
+  if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of softmax scratch");
+  e = attn::launch_softmax_split(x, y, M, N, (int)c, static_cast<attn::DType>(dtype),
+                                 static_cast<float*>(scratch), s);
+  const hipError_t ef = hipFreeAsync(scratch, s);
+  if (e != hipSuccess) return hip_fail(e, "softmax kernel launch");
+  if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of softmax scratch");
+  return ATTN_OK;
 }
 
 const char* attn_strerror(int code) {

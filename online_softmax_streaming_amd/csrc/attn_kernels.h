@@ -48,6 +48,13 @@ hipError_t launch_merge_batch(const float* m1, const float* l1, const float* m2,
                               const float* l2, float* m, float* l, int64_t n,
                               hipStream_t stream);
 
+// Wide-row split softmax (softmax_split.hip): chunks per row, scratch bytes
+// (FP32 (m, l) per chunk and per row) and the three ordered kernels.
+int64_t softmax_chunks(int64_t N, int64_t C);
+int64_t softmax_scratch_bytes(int64_t M, int64_t N, int64_t C);
+hipError_t launch_softmax_split(const void* x, void* y, int64_t M, int64_t N, int C, DType dtype,
+                                float* scratch, hipStream_t stream);
+
 // Row count above which attn_fwd takes the prefill kernels.
 constexpr int64_t kDecodeMaxNq = 8;
 

@@ -1,6 +1,6 @@
 """Seeded synthetic workloads: shapes and input generators.
 
-Holds none of the attention arithmetic; it only names the workloads and
+Holds none of the attention or softmax arithmetic; it only names the workloads and
 draws their inputs, so both the HIP path and the oracle can be fed the same
 tensors.  Recipe: Q, K, V ~ N(0, 1) as float32 from one seeded torch
 generator, drawn in the order Q, K, V, then rounded to the workload's dtype.
@@ -94,3 +94,37 @@ def make_qkv(w, seed=0, device="cpu"):
 def random_qkv(B, H, Nq, Nk, D, dtype, seed=0, device="cpu", k_ramp=0.0):
     """Same recipe for an ad-hoc shape."""
     return make_qkv(Workload("adhoc", B, H, Nq, Nk, D, dtype, False, k_ramp), seed, device)
+
+
+@dataclasses.dataclass(frozen=True)
+class SoftmaxWorkload:
+    """A wide-row softmax input: x ~ 3 * N(0, 1) float32, rounded to dtype."""
+    name: str
+    M: int
+    N: int
+    dtype: str
+
+    @property
+    def torch_dtype(self):
+        return DTYPES[self.dtype]
+
+    def bytes(self):
+        """HBM bytes the split method moves: x read twice (partial pass and
+        normalising pass), y written once.  A single-pass method would need
+        two of these three."""
+        el = torch.finfo(self.torch_dtype).bits // 8
+        return 3 * el * self.M * self.N
+
+
+SOFTMAX_WORKLOADS = {w.name: w for w in [
+    # The pages' widest row (131072 columns), 1024 rows: 256 MiB of bf16.
+    SoftmaxWorkload("wide_softmax_bf16", 1024, 131072, "bf16"),
+]}
+
+
+def make_softmax_input(w, seed=0, device="cpu"):
+    """x for softmax workload ``w`` from ``seed`` (generated on ``device``)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn((w.M, w.N), generator=g, dtype=torch.float32, device=device) * 3.0
+    return x.to(w.torch_dtype)

@@ -162,3 +162,58 @@ def test_merge_batch_rejects_bad_sizes(attn):
     assert L.online_merge_batch(p, p, p, p, p, p, 0, None) == 0
     assert L.online_merge_batch(None, p, p, p, p, p, 4, None) == 1
     assert L.online_merge_batch(ctypes.c_void_p(0x1001), p, p, p, p, p, 4, None) == 1
+
+
+# --------------------------------------------------------------------------
+# Split softmax: host-side sizing and argument checks (no kernel launched).
+
+def test_softmax_scratch_worked_example(attn):
+    # Answer-key page, worked answer A2: M=4, N=32769, C=1024 -> T=33 chunks,
+    # 8*4*(33+1) = 1088 bytes of scratch.
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "worked_examples.json")))["a2_scratch"]
+    assert attn.softmax_rows_scratch_bytes(g["M"], g["N"], g["chunk"]) == g["expected_scratch_bytes"]
+
+
+@pytest.mark.parametrize("m,n,c", [(1, 1, 256), (3, 256, 256), (3, 257, 256), (2, 131072, 4096),
+                                   (0, 5, 1024), (7, 100000, 512)])
+def test_softmax_scratch_matches_oracle_formula(attn, m, n, c):
+    from oracle import scratch_bytes
+    assert attn.softmax_rows_scratch_bytes(m, n, c) == scratch_bytes(m, n, c)
+
+
+def test_softmax_scratch_auto_chunk_is_a_listed_size(attn):
+    from oracle import scratch_bytes
+    for m, n in ((1, 131072), (4096, 4096), (4, 32769), (100000, 300)):
+        got = attn.softmax_rows_scratch_bytes(m, n, 0)
+        assert got in {scratch_bytes(m, n, c) for c in (256, 512, 1024, 2048, 4096)}
+
+
+@pytest.mark.parametrize("m,n,c", [(-1, 5, 256), (2, 0, 256), (2, 5, 100), (2, 5, 8192)])
+def test_softmax_scratch_rejects_bad_sizes(attn, m, n, c):
+    assert attn.softmax_rows_scratch_bytes(m, n, c) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), 1),
+    (dict(M=-1), 1),
+    (dict(N=0), 1),
+    (dict(chunk=300), 1),
+    (dict(x=0), 1),
+    (dict(y=0), 1),
+    (dict(x=17), 1),              # not aligned to the element size
+    (dict(y=4104), 1),            # overlaps x without being x
+    (dict(M=1 << 31, N=4096, chunk=256, y=4096), 2),  # in place; too many chunks for one grid
+])
+def test_softmax_rows_rejects_bad_arguments(attn, kw, code):
+    from online_softmax_streaming_amd import _lib
+    args = dict(x=4096, y=1 << 30, M=4, N=1024, chunk=256, dtype=2, stream=None)
+    args.update(kw)
+    rc = _lib.lib().softmax_rows(args["x"], args["y"], args["M"], args["N"], args["chunk"],
+                                 args["dtype"], args["stream"])
+    assert rc == code, _lib.lib().attn_last_error()
+
+
+def test_softmax_rows_empty_is_a_noop(attn):
+    from online_softmax_streaming_amd import _lib
+    assert _lib.lib().softmax_rows(None, None, 0, 1024, 0, 2, None) == 0

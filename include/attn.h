@@ -113,6 +113,21 @@ ATTN_API int attn_fwd_stats(const void* Q, const void* K, const void* V, void* o
                    float* m_out, float* l_out, void* stream);
 
 /*
+ * attn_fwd_gqa -- attn_fwd_stats with grouped K/V heads (grouped-query
+ * attention): K and V are contiguous [B, Hkv, Nk, D] with Hkv dividing H,
+ * and query head h attends with K/V head h / (H / Hkv).  Hkv == H is
+ * attn_fwd_stats exactly.  m_out and l_out may each be NULL.  The pages
+ * attend one head at a time; grouping only changes which K/V head a query
+ * head reads, so the same streaming computation ([AK] row A3) runs per
+ * head.  Errors as attn_fwd, plus ATTN_E_INVALID if Hkv < 1 or Hkv does not
+ * divide H (for H > 0).
+ */
+ATTN_API int attn_fwd_gqa(const void* Q, const void* K, const void* V, void* out,
+                          int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk,
+                          int64_t D, int causal, float scale, int dtype,
+                          float* m_out, float* l_out, void* stream);
+
+/*
  * online_merge -- merge two A1 summaries ([AK] row A1 and its worked answer).
  *
  * A state (m, l) stands for sum_j exp(x_j) = l * exp(m); (-inf, 0) is the

@@ -16,6 +16,7 @@ from .attn import (  # noqa: F401
     ATTN_OK,
     AttnError,
     attn_fwd,
+    attn_fwd_gqa,
     attn_fwd_raw,
     attn_fwd_stats,
     attn_strerror,

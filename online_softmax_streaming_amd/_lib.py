@@ -25,6 +25,9 @@ SIGNATURES = {
     "attn_fwd_stats": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64,
                                       _c_i64, _c_i64, ctypes.c_int, ctypes.c_float, ctypes.c_int,
                                       _c_ptr, _c_ptr, _c_ptr]),
+    "attn_fwd_gqa": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_i64,
+                                    _c_i64, _c_i64, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                    _c_ptr, _c_ptr, _c_ptr]),
     "online_merge": (ctypes.c_int, [ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                     ctypes.c_double, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_double)]),

@@ -51,7 +51,7 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _validate(q, k, v):
+def _validate(q, k, v, grouped=False):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
@@ -70,12 +70,17 @@ def _validate(q, k, v):
     if k.shape != v.shape:
         raise ValueError(f"k and v shapes differ: {tuple(k.shape)} vs {tuple(v.shape)}")
     b, h, _, d = q.shape
-    if (k.shape[0], k.shape[1], k.shape[3]) != (b, h, d):
+    if grouped:
+        hkv = k.shape[1]
+        if (k.shape[0], k.shape[3]) != (b, d) or hkv < 1 or h % hkv:
+            raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)}: need equal B and D "
+                             "and K/V heads dividing the query heads")
+    elif (k.shape[0], k.shape[1], k.shape[3]) != (b, h, d):
         raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree on B, H or D")
 
 
 def attn_fwd_stats(q, k, v, causal=False, scale=None, out=None, m_out=None, l_out=None,
-                   stream=None, want_stats=True):
+                   stream=None, want_stats=True, _grouped=False):
     """Streaming attention forward; returns (out, m, l).
 
     q: [B, H, Nq, D]; k, v: [B, H, Nk, D]; one dtype (float32, float16 or
@@ -84,7 +89,7 @@ def attn_fwd_stats(q, k, v, causal=False, scale=None, out=None, m_out=None, l_ou
     given.  ``scale`` defaults to FP32(1/sqrt(D)).  The work is queued on
     ``stream`` (default: torch's current stream of q's device).
     """
-    _validate(q, k, v)
+    _validate(q, k, v, grouped=_grouped)
     b, h, nq, d = q.shape
     nk = k.shape[2]
     if scale is None:
@@ -108,13 +113,27 @@ def attn_fwd_stats(q, k, v, causal=False, scale=None, out=None, m_out=None, l_ou
         args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                 ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
                 b, h, nq, nk, d, int(bool(causal)), float(scale), _DTYPES[q.dtype])
-        if want_stats:
+        if _grouped:
+            gargs = args[:6] + (k.shape[1],) + args[6:]
+            stats = ((ctypes.c_void_p(m_out.data_ptr()), ctypes.c_void_p(l_out.data_ptr()))
+                     if want_stats else (None, None))
+            _check(lib().attn_fwd_gqa(*gargs, *stats, sh), "attn_fwd_gqa")
+        elif want_stats:
             rc = lib().attn_fwd_stats(*args, ctypes.c_void_p(m_out.data_ptr()),
                                       ctypes.c_void_p(l_out.data_ptr()), sh)
             _check(rc, "attn_fwd_stats")
         else:
             _check(lib().attn_fwd(*args, sh), "attn_fwd")
     return out, m_out, l_out
+
+
+def attn_fwd_gqa(q, k, v, causal=False, scale=None, out=None, m_out=None, l_out=None,
+                 stream=None, want_stats=False):
+    """Grouped-query attention forward: k, v are [B, Hkv, Nk, D] with Hkv
+    dividing H, and query head h attends with K/V head h // (H // Hkv).
+    Returns (out, m, l); m and l are None unless ``want_stats``."""
+    return attn_fwd_stats(q, k, v, causal=causal, scale=scale, out=out, m_out=m_out,
+                          l_out=l_out, stream=stream, want_stats=want_stats, _grouped=True)
 
 
 def attn_fwd(q, k, v, causal=False, scale=None, out=None, stream=None):

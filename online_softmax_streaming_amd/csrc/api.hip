@@ -59,8 +59,8 @@ void keep_pool_memory() {
 }
 
 int run_attention(const void* Q, const void* K, const void* V, void* out, int64_t B, int64_t H,
-                  int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, int dtype,
-                  float* m_out, float* l_out, void* stream) {
+                  int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
+                  int dtype, float* m_out, float* l_out, void* stream) {
   g_last_error[0] = '\0';
   if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16)
     return fail(ATTN_E_INVALID, "dtype %d is not ATTN_F32, ATTN_F16 or ATTN_BF16", dtype);
@@ -68,6 +68,8 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
     return fail(ATTN_E_INVALID, "negative size (B=%lld H=%lld Nq=%lld Nk=%lld)", (long long)B,
                 (long long)H, (long long)Nq, (long long)Nk);
+  if (H > 0 && (Hkv < 1 || Hkv > H || H % Hkv != 0))
+    return fail(ATTN_E_INVALID, "Hkv=%lld must divide H=%lld", (long long)Hkv, (long long)H);
   if (D <= 0) return fail(ATTN_E_INVALID, "D must be positive, got %lld", (long long)D);
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(ATTN_E_INVALID, "scale must be finite and > 0, got %g", (double)scale);
@@ -87,7 +89,7 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
   if ((m_out && !aligned(m_out, 4)) || (l_out && !aligned(l_out, 4)))
     return fail(ATTN_E_INVALID, "m_out and l_out must be 4-byte aligned");
   const int64_t qbytes = B * H * Nq * D * elem;
-  const int64_t kbytes = B * H * Nk * D * elem;
+  const int64_t kbytes = B * Hkv * Nk * D * elem;
   const int64_t sbytes = B * H * Nq * 4;
   if (overlaps(out, qbytes, Q, qbytes) || overlaps(out, qbytes, K, kbytes) ||
       overlaps(out, qbytes, V, kbytes))
@@ -105,6 +107,7 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
   p.l_out = l_out;
   p.B = B;
   p.H = H;
+  p.Hkv = Hkv;
   p.Nq = Nq;
   p.Nk = Nk;
   p.D = D;
@@ -154,14 +157,22 @@ extern "C" {
 
 int attn_fwd(const void* Q, const void* K, const void* V, void* out, int64_t B, int64_t H,
              int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, int dtype, void* stream) {
-  return run_attention(Q, K, V, out, B, H, Nq, Nk, D, causal, scale, dtype, nullptr, nullptr,
+  return run_attention(Q, K, V, out, B, H, H, Nq, Nk, D, causal, scale, dtype, nullptr, nullptr,
                        stream);
 }
 
 int attn_fwd_stats(const void* Q, const void* K, const void* V, void* out, int64_t B, int64_t H,
                    int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, int dtype,
                    float* m_out, float* l_out, void* stream) {
-  return run_attention(Q, K, V, out, B, H, Nq, Nk, D, causal, scale, dtype, m_out, l_out, stream);
+  return run_attention(Q, K, V, out, B, H, H, Nq, Nk, D, causal, scale, dtype, m_out, l_out,
+                       stream);
+}
+
+int attn_fwd_gqa(const void* Q, const void* K, const void* V, void* out, int64_t B, int64_t H,
+                 int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
+                 int dtype, float* m_out, float* l_out, void* stream) {
+  return run_attention(Q, K, V, out, B, H, Hkv, Nq, Nk, D, causal, scale, dtype, m_out, l_out,
+                       stream);
 }
 
 int online_merge(double m1, double l1, double m2, double l2, double* m, double* l) {

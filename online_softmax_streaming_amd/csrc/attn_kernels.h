@@ -19,6 +19,7 @@ struct Problem {
   float* m_out;  // optional [B*H*Nq]
   float* l_out;  // optional [B*H*Nq]
   int64_t B, H, Nq, Nk, D;
+  int64_t Hkv;  // K/V heads; query head h reads K/V head h / (H / Hkv)
   bool causal;
   float scale;
   DType dtype;

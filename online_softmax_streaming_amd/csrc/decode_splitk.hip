@@ -35,6 +35,7 @@ struct DecodeArgs {
   float* l_out;
   float* part;  // [rows][S][D + 2]: m, l, a[D]
   int H, Nq, Nk;
+  int group;  // query heads per K/V head
   int S;
   int kps;  // keys per split
   float c;  // scale * log2(e)
@@ -68,8 +69,9 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
   const int sub = tid - g * LPR;
   const float c = a.c;
 
-  const T* __restrict__ Kh = static_cast<const T*>(a.k) + (int64_t)bh * Nk * D;
-  const T* __restrict__ Vh = static_cast<const T*>(a.v) + (int64_t)bh * Nk * D;
+  // Query head (b, h) reads K/V head (b, h / group): bh / group.
+  const T* __restrict__ Kh = static_cast<const T*>(a.k) + (int64_t)(bh / a.group) * Nk * D;
+  const T* __restrict__ Vh = static_cast<const T*>(a.v) + (int64_t)(bh / a.group) * Nk * D;
 
   float qv[VEC];
   {
@@ -191,6 +193,7 @@ hipError_t launch_typed(const Problem& p, const DecodePlan& plan, float* scratch
   a.l_out = p.l_out;
   a.part = scratch;
   a.H = (int)p.H;
+  a.group = (int)(p.H / p.Hkv);
   a.Nq = (int)p.Nq;
   a.Nk = (int)p.Nk;
   a.S = plan.splits;

@@ -27,6 +27,7 @@ struct F32Args {
   float* l_out;
   int Nq, Nk;
   int nqt;
+  int group;  // query heads per K/V head
   float c;  // scale * log2(e)
 };
 
@@ -47,8 +48,8 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
   const int qt = blockIdx.x - bh * a.nqt;
   const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
   const float* __restrict__ Qh = a.q + (int64_t)bh * Nq * D;
-  const float* __restrict__ Kh = a.k + (int64_t)bh * Nk * D;
-  const float* __restrict__ Vh = a.v + (int64_t)bh * Nk * D;
+  const float* __restrict__ Kh = a.k + (int64_t)(bh / a.group) * Nk * D;  // K/V head bh / group
+  const float* __restrict__ Vh = a.v + (int64_t)(bh / a.group) * Nk * D;
   float* __restrict__ Oh = a.o + (int64_t)bh * Nq * D;
 
   const int tid = threadIdx.x;
@@ -147,6 +148,7 @@ hipError_t launch_typed(const Problem& p) {
   a.Nq = (int)p.Nq;
   a.Nk = (int)p.Nk;
   a.nqt = (int)((p.Nq + QPB - 1) / QPB);
+  a.group = (int)(p.H / p.Hkv);
   a.c = p.scale * kLog2e;
   const int64_t grid = p.B * p.H * a.nqt;
   hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,

@@ -92,6 +92,7 @@ struct PrefillArgs {
   float* m_out;
   float* l_out;
   int Nq, Nk;
+  int group;    // query heads per K/V head
   int nqt;      // query tiles per (b, h)
   int nwork;    // workgroups per (b, h): nqt, or ceil(nqt / 2) paired causal tiles
   int total;    // (B*H) * nwork real workgroups
@@ -192,8 +193,9 @@ void prefill_mfma_kernel(PrefillArgs a) {
 
     const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
     const T* __restrict__ Qh = static_cast<const T*>(a.q) + (int64_t)bh * Nq * D;
-    const T* Kh = static_cast<const T*>(a.k) + (int64_t)bh * Nk * D;
-    const T* Vh = static_cast<const T*>(a.v) + (int64_t)bh * Nk * D;
+    // Query head (b, h) reads K/V head (b, h / group): bh / group.
+    const T* Kh = static_cast<const T*>(a.k) + (int64_t)(bh / a.group) * Nk * D;
+    const T* Vh = static_cast<const T*>(a.v) + (int64_t)(bh / a.group) * Nk * D;
     T* __restrict__ Oh = static_cast<T*>(a.o) + (int64_t)bh * Nq * D;
 
     const int tid = threadIdx.x;
@@ -459,6 +461,7 @@ hipError_t launch_typed(const Problem& p) {
   a.l_out = p.l_out;
   a.Nq = (int)p.Nq;
   a.Nk = (int)p.Nk;
+  a.group = (int)(p.H / p.Hkv);
   a.nqt = (int)((p.Nq + BM - 1) / BM);
   a.nwork = CAUSAL ? (a.nqt + 1) / 2 : a.nqt;
   const int64_t total = p.B * p.H * a.nwork;

@@ -217,3 +217,12 @@ def test_softmax_rows_rejects_bad_arguments(attn, kw, code):
 def test_softmax_rows_empty_is_a_noop(attn):
     from online_softmax_streaming_amd import _lib
     assert _lib.lib().softmax_rows(None, None, 0, 1024, 0, 2, None) == 0
+
+
+@pytest.mark.parametrize("hkv", [0, -1, 3, 16])
+def test_attn_fwd_gqa_rejects_bad_group(attn, hkv):
+    from online_softmax_streaming_amd import _lib
+    rc = _lib.lib().attn_fwd_gqa(4096, 8192, 12288, 1 << 30, 1, 8, hkv, 64, 64, 64, 0, 0.125, 2,
+                                 None, None, None)
+    assert rc == 1, _lib.lib().attn_last_error()
+    assert b"Hkv" in _lib.lib().attn_last_error()

@@ -1,0 +1,79 @@
+"""GPU parity of grouped-query attention (attn_fwd_gqa).
+
+K and V carry Hkv heads and query head h reads K/V head h // (H // Hkv).
+The oracle is the plain definition applied to K/V with each head repeated
+H // Hkv times (oracle.attention on the expanded tensors).  Tolerances are
+the attention tolerances of the other parity tests.  The same kernels run
+with only the K/V head index changed, so the grouped call must also equal,
+bit for bit, attn_fwd on explicitly repeated K/V.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from online_softmax_streaming_amd.workloads import random_qkv
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2}
+LSE_TOL = {"f32": 1e-5, "f16": 2.0 ** -11 + 1e-5, "bf16": 2.0 ** -8 + 1e-5}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import online_softmax_streaming_amd as m
+    return m
+
+
+def _grouped(b, h, hkv, nq, nk, d, dtype, seed):
+    q, _, _ = random_qkv(b, h, nq, nk, d, dtype, seed=seed, device="cuda")
+    _, k, v = random_qkv(b, hkv, nq, nk, d, dtype, seed=seed + 1, device="cuda", k_ramp=0.01)
+    return q, k, v
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("h,hkv,nq,nk,d", [
+    (8, 1, 300, 300, 64), (8, 2, 259, 517, 128), (8, 4, 517, 259, 64), (6, 3, 1, 1000, 128),
+    (8, 2, 5, 700, 64), (4, 4, 129, 129, 32),
+])
+def test_parity(lib, dtype, causal, h, hkv, nq, nk, d):
+    q, k, v = _grouped(2, h, hkv, nq, nk, d, dtype, seed=h * 10 + hkv + nq)
+    out, m, l = lib.attn_fwd_gqa(q, k, v, causal=causal, want_stats=True)
+    torch.cuda.synchronize()
+    g = h // hkv
+    qd = q.cpu().double().numpy()
+    kd = np.repeat(k.cpu().double().numpy(), g, axis=1)
+    vd = np.repeat(v.cpu().double().numpy(), g, axis=1)
+    scale = lib.default_scale(d)
+    want, wm, wl = oracle.attention(qd, kd, vd, causal, scale)
+    err = np.max(np.abs(out.cpu().double().numpy() - want))
+    assert err <= TOL[dtype], err
+    with np.errstate(divide="ignore"):  # rows with no visible key: l = 0, lse = -inf
+        lse = m.cpu().double().numpy() + np.log(l.cpu().double().numpy())
+        wlse = wm + np.log(wl)
+    fin = np.isfinite(wlse)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.max(np.abs(lse[fin] - wlse[fin]), initial=0.0) <= LSE_TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("nq", [1, 300])
+def test_equals_mha_on_repeated_kv(lib, dtype, nq):
+    q, k, v = _grouped(2, 8, 2, nq, 640, 128, dtype, seed=77)
+    got = lib.attn_fwd_gqa(q, k, v, causal=True)[0]
+    kr = k.repeat_interleave(4, dim=1).contiguous()
+    vr = v.repeat_interleave(4, dim=1).contiguous()
+    want = lib.attn_fwd(q, kr, vr, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+
+
+def test_hkv_equal_h_is_attn_fwd_stats(lib):
+    q, k, v = random_qkv(1, 4, 200, 333, 64, "f16", seed=3, device="cuda")
+    a, am, al = lib.attn_fwd_gqa(q, k, v, causal=True, want_stats=True)
+    b, bm, bl = lib.attn_fwd_stats(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(am, bm) and torch.equal(al, bl)

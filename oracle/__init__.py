@@ -1,4 +1,5 @@
-"""FP64 CPU oracle for streaming (online-softmax) attention and row softmax.
+"""FP64 CPU oracle for streaming (online-softmax) attention (forward and
+backward) and row softmax.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 load anything from this package: only ``tests/``, ``__graft_entry__.smoke()``
@@ -9,17 +10,18 @@ constants or helpers with the HIP library under
 Sources (three web pages on one subject):
   * "Intermediate and advanced kernel workshops" (the workshops page):
     section "Scope and contracts" -- the streaming_attention and
-    split_softmax contracts.
+    split_softmax contracts; the I2 softmax-backward workshop.
   * "Compare reasoning after your own attempt" (the answer-key page):
-    the A1 / A2 / A3 rows of its table, "Worked answers worth memorizing by
-    derivation" (A1 merge, A2 scratch size, A3 six/seven example) and the
+    the I2 / A1 / A2 / A3 rows of its table, "Worked answers worth memorizing
+    by derivation" (I2 VJP, A1 merge, A2 scratch size, A3 six/seven) and the
     closing note that the attention oracle materialises FP64 scores.
   * "Kernel Notes & Checklist": section 4, "The gotchas ledger" (-inf padding
     before a max, 0 before a sum, ghost rows pinned so they cannot give NaN).
 
-Every function here is pinned by ``tests/test_oracle_pins.py`` and
-``tests/test_softmax_oracle_pins.py`` against values the pages print, closed
-forms, invariants, library routines and 50-digit brute force.
+Every function here is pinned by ``tests/test_oracle_pins.py``,
+``tests/test_softmax_oracle_pins.py`` and ``tests/test_backward_oracle_pins.py``
+against values the pages print, closed forms, invariants, library routines,
+finite differences and 50-digit brute force.
 """
 
 from .attention import (  # noqa: F401
@@ -36,4 +38,10 @@ from .softmax import (  # noqa: F401
     scratch_bytes,
     softmax_rows,
     split_softmax_model,
+)
+from .attention_backward import (  # noqa: F401
+    attention_backward,
+    attention_backward_head,
+    probabilities,
+    softmax_vjp,
 )

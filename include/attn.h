@@ -128,6 +128,53 @@ ATTN_API int attn_fwd_gqa(const void* Q, const void* K, const void* V, void* out
                           float* m_out, float* l_out, void* stream);
 
 /*
+ * attn_bwd -- gradients of the attention forward (dQ, dK, dV), recomputing
+ * the probabilities from each row's forward state instead of storing them.
+ *
+ * For out = attn_fwd_gqa(Q, K, V) with row states (m, l) and an upstream
+ * gradient dO of out, per batch b, query head h, K/V head h / (H / Hkv):
+ *     P  = exp(scale * Q K^T - lse) on visible keys (0 elsewhere), lse = m + ln l
+ *     dV = sum over the query heads of the group of P^T dO
+ *     dS = P * (dO V^T - Delta),  Delta[i] = sum_d dO[i, d] * O[i, d]
+ *     dQ = scale * dS K,  dK = sum over the group of scale * dS^T Q
+ * dS row by row is the softmax vector-Jacobian product y * (g - <y, g>) of
+ * [W]'s intermediate workshop I2 (softmax backward; [AK] row I2 and its
+ * worked answer), with y = P and g = dO V^T; <P, dO V^T> = Delta because
+ * out = P V.  Visibility (causal or not) is attn_fwd's; a query row with no
+ * visible key gets dQ = 0, a key no query sees gets dK = dV = 0.
+ *
+ * Layout: Q, O, dO, dQ contiguous [B, H, Nq, D]; K, V, dK, dV contiguous
+ * [B, Hkv, Nk, D]; m, l FP32 [B, H, Nq] exactly as attn_fwd_stats /
+ * attn_fwd_gqa write them (O too: the forward's rounded output).  All
+ * tensors but m, l use `dtype`, which must be ATTN_F16 or ATTN_BF16
+ * (ATTN_F32 returns ATTN_E_UNSUPPORTED).  Arithmetic: Q K^T, dO V^T and every
+ * sum in FP32 on bf16/f16 matrix cores; P and dS are rounded to `dtype` as
+ * operands of the products that form dV, dK and dQ; one round-to-nearest-
+ * even cast per output element.  No atomics: results are bitwise
+ * reproducible from run to run.
+ *
+ * Arguments:
+ *   Q, K, V, O, dO  device pointers, 16-byte aligned (K, V may be NULL if
+ *                   Nk == 0; Q, O, dO, m, l may be NULL if Nq == 0).
+ *   m, l            device FP32 arrays, 4-byte aligned.
+ *   dQ, dK, dV      device outputs, 16-byte aligned, overwritten entirely;
+ *                   none may overlap an input or another output.
+ *   B, H, Hkv, Nq, Nk, D, causal, scale, dtype, stream: as attn_fwd_gqa
+ *                   (D in {16, 32, 64, 128}); additionally B*Hkv*Nk < 2^31.
+ *                   Nq == 0 writes dK = dV = 0; Nk == 0 writes dQ = 0.
+ * Memory: a scratch array of 8 * B*H*Nq bytes (per row the base-2 lse and
+ * Delta), taken with hipMallocAsync and released with hipFreeAsync on
+ * `stream`.  Two kernels are queued: dQ (which also fills the scratch),
+ * then dK and dV.
+ * Returns ATTN_OK once queued, else the status codes of attn_fwd.
+ */
+ATTN_API int attn_bwd(const void* Q, const void* K, const void* V, const void* O,
+                      const void* dO, const float* m, const float* l,
+                      void* dQ, void* dK, void* dV,
+                      int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk,
+                      int64_t D, int causal, float scale, int dtype, void* stream);
+
+/*
  * online_merge -- merge two A1 summaries ([AK] row A1 and its worked answer).
  *
  * A state (m, l) stands for sum_j exp(x_j) = l * exp(m); (-inf, 0) is the

@@ -1,5 +1,5 @@
-"""Streaming (online-softmax) attention forward and wide-row split softmax
-for AMD MI355X (gfx950).
+"""Streaming (online-softmax) attention forward and backward, and wide-row
+split softmax, for AMD MI355X (gfx950).
 
 The computation lives in the HIP library libattn.so (C ABI in
 include/attn.h); this package is its Python binding plus the seeded
@@ -15,6 +15,7 @@ from .attn import (  # noqa: F401
     ATTN_F32,
     ATTN_OK,
     AttnError,
+    attn_bwd,
     attn_fwd,
     attn_fwd_gqa,
     attn_fwd_raw,

@@ -28,6 +28,8 @@ SIGNATURES = {
     "attn_fwd_gqa": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_i64,
                                     _c_i64, _c_i64, ctypes.c_int, ctypes.c_float, ctypes.c_int,
                                     _c_ptr, _c_ptr, _c_ptr]),
+    "attn_bwd": (ctypes.c_int, [_c_ptr] * 10 + [_c_i64] * 6 + [ctypes.c_int, ctypes.c_float,
+                                                                 ctypes.c_int, _c_ptr]),
     "online_merge": (ctypes.c_int, [ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                     ctypes.c_double, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_double)]),

@@ -142,6 +142,45 @@ def attn_fwd(q, k, v, causal=False, scale=None, out=None, stream=None):
                           want_stats=False)[0]
 
 
+def attn_bwd(q, k, v, out, dout, m, l, causal=False, scale=None, dq=None, dk=None, dv=None,
+             stream=None):
+    """Attention backward; returns (dq, dk, dv).
+
+    q, out, dout: [B, H, Nq, D]; k, v: [B, Hkv, Nk, D] (Hkv dividing H);
+    float16 or bfloat16, contiguous, on one GPU.  ``out``, ``m`` and ``l``
+    are what attn_fwd_stats / attn_fwd_gqa returned for the same inputs
+    (m, l: float32 [B, H, Nq]).  ``scale`` defaults to FP32(1/sqrt(D)) and
+    must be the forward's.  Outputs are allocated when not given.
+    """
+    _validate(q, k, v, grouped=True)
+    b, h, nq, d = q.shape
+    hkv, nk = k.shape[1], k.shape[2]
+    for name, t in (("out", out), ("dout", dout)):
+        if (not isinstance(t, torch.Tensor) or t.shape != q.shape or t.dtype != q.dtype
+                or t.device != q.device or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    for name, t in (("m", m), ("l", l)):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device != q.device
+                or t.shape != (b, h, nq) or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 [B, H, Nq] GPU tensor")
+    if scale is None:
+        scale = default_scale(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous tensor like {'q' if like is q else 'k'}")
+    with torch.cuda.device(q.device):
+        sh = _stream_handle(stream, q.device)
+        ptrs = (ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out, dout, m, l, dq, dk, dv))
+        rc = lib().attn_bwd(*ptrs, b, h, hkv, nq, nk, d, int(bool(causal)), float(scale),
+                            _DTYPES[q.dtype], sh)
+    _check(rc, "attn_bwd")
+    return dq, dk, dv
+
+
 def attn_fwd_raw(q_ptr, k_ptr, v_ptr, out_ptr, b, h, nq, nk, d, causal, scale, dtype,
                  stream_handle=0):
     """Direct C call with raw device pointers; returns the status code."""

@@ -175,6 +175,99 @@ int attn_fwd_gqa(const void* Q, const void* K, const void* V, void* out, int64_t
                        stream);
 }
 
+int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* m, const float* l, void* dQ, void* dK, void* dV, int64_t B, int64_t H,
+             int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, int dtype,
+             void* stream) {
+  g_last_error[0] = '\0';
+  if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_E_INVALID, "dtype %d is not ATTN_F32, ATTN_F16 or ATTN_BF16", dtype);
+  if (causal != 0 && causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1, got %d", causal);
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+    return fail(ATTN_E_INVALID, "negative size (B=%lld H=%lld Nq=%lld Nk=%lld)", (long long)B,
+                (long long)H, (long long)Nq, (long long)Nk);
+  if (H > 0 && (Hkv < 1 || Hkv > H || H % Hkv != 0))
+    return fail(ATTN_E_INVALID, "Hkv=%lld must divide H=%lld", (long long)Hkv, (long long)H);
+  if (D <= 0) return fail(ATTN_E_INVALID, "D must be positive, got %lld", (long long)D);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(ATTN_E_INVALID, "scale must be finite and > 0, got %g", (double)scale);
+  if (dtype == ATTN_F32)
+    return fail(ATTN_E_UNSUPPORTED, "attn_bwd: FP32 inputs not built (F16 and BF16 are)");
+  if (D != 16 && D != 32 && D != 64 && D != 128)
+    return fail(ATTN_E_UNSUPPORTED, "head size D=%lld not built (16, 32, 64, 128)", (long long)D);
+  if (B > kI32Max || H > kI32Max || Nq > kI32Max || Nk > kI32Max || B * H > kI32Max ||
+      Nq * D > kI32Max || Nk * D > kI32Max || B * H * Nq > kI32Max || B * Hkv * Nk > kI32Max)
+    return fail(ATTN_E_INVALID, "sizes exceed the 32-bit limits (B*H, Nq*D, Nk*D, B*H*Nq, "
+                                "B*Hkv*Nk < 2^31)");
+  if (B == 0 || H == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
+
+  const int64_t elem = 2;
+  const int64_t qbytes = B * H * Nq * D * elem;
+  const int64_t kbytes = B * Hkv * Nk * D * elem;
+  const int64_t sbytes = B * H * Nq * 4;
+  if (Nq > 0 && (!Q || !O || !dO || !m || !l || !dQ))
+    return fail(ATTN_E_INVALID, "Q, O, dO, m, l and dQ must be non-NULL when Nq > 0");
+  if (Nk > 0 && (!K || !V || !dK || !dV))
+    return fail(ATTN_E_INVALID, "K, V, dK and dV must be non-NULL when Nk > 0");
+  const void* a16[8] = {Q, K, V, O, dO, dQ, dK, dV};
+  for (const void* p : a16)
+    if (p && !aligned(p, 16)) return fail(ATTN_E_INVALID, "Q, K, V, O, dO, dQ, dK, dV must be 16-byte aligned");
+  if ((m && !aligned(m, 4)) || (l && !aligned(l, 4)))
+    return fail(ATTN_E_INVALID, "m and l must be 4-byte aligned");
+  // Outputs must not overlap any input or each other.
+  struct Span {
+    const void* p;
+    int64_t n;
+  };
+  const Span outs[3] = {{dQ, Nq > 0 ? qbytes : 0}, {dK, kbytes}, {dV, kbytes}};
+  const Span ins[7] = {{Q, qbytes}, {K, kbytes}, {V, kbytes}, {O, qbytes},
+                       {dO, qbytes}, {m, sbytes}, {l, sbytes}};
+  for (int i = 0; i < 3; ++i) {
+    for (const Span& in : ins)
+      if (overlaps(outs[i].p, outs[i].n, in.p, in.n))
+        return fail(ATTN_E_INVALID, "dQ, dK and dV must not overlap an input");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+        return fail(ATTN_E_INVALID, "dQ, dK and dV must not overlap each other");
+  }
+
+  attn::BwdProblem p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.dout = dO;
+  p.m = m;
+  p.l = l;
+  p.dq = dQ;
+  p.dk = dK;
+  p.dv = dV;
+  p.B = B;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.D = D;
+  p.causal = causal != 0;
+  p.scale = scale;
+  p.dtype = static_cast<attn::DType>(dtype);
+  p.stream = static_cast<hipStream_t>(stream);
+
+  const size_t sb = attn::bwd_scratch_bytes(p);
+  void* scratch = nullptr;
+  hipError_t e;
+  if (sb > 0) {
+    keep_pool_memory();
+    e = hipMallocAsync(&scratch, sb, p.stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of backward scratch");
+  }
+  e = attn::launch_bwd_mfma(p, static_cast<float*>(scratch));
+  const hipError_t ef = scratch ? hipFreeAsync(scratch, p.stream) : hipSuccess;
+  if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
+  if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of backward scratch");
+  return ATTN_OK;
+}
+
 int online_merge(double m1, double l1, double m2, double l2, double* m, double* l) {
   g_last_error[0] = '\0';
   if (!m || !l) return fail(ATTN_E_INVALID, "online_merge: m and l must be non-NULL");

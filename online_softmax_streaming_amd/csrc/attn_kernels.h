@@ -56,6 +56,29 @@ int64_t softmax_scratch_bytes(int64_t M, int64_t N, int64_t C);
 hipError_t launch_softmax_split(const void* x, void* y, int64_t M, int64_t N, int C, DType dtype,
                                 float* scratch, hipStream_t stream);
 
+// Attention backward on bf16/f16 matrix cores (bwd_mfma.hip): a dQ kernel
+// that also writes each row's (base-2 lse, Delta) to `scratch`, then a
+// dK/dV kernel that reads them, on p.stream.
+struct BwdProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* m;  // [B*H*Nq] forward row state, natural units
+  const float* l;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t B, H, Hkv, Nq, Nk, D;
+  bool causal;
+  float scale;
+  DType dtype;
+  hipStream_t stream;
+};
+size_t bwd_scratch_bytes(const BwdProblem& p);
+hipError_t launch_bwd_mfma(const BwdProblem& p, float* scratch);
+
 // Row count above which attn_fwd takes the prefill kernels.
 constexpr int64_t kDecodeMaxNq = 8;
 

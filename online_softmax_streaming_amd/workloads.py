@@ -96,6 +96,16 @@ def random_qkv(B, H, Nq, Nk, D, dtype, seed=0, device="cpu", k_ramp=0.0):
     return make_qkv(Workload("adhoc", B, H, Nq, Nk, D, dtype, False, k_ramp), seed, device)
 
 
+def random_dout(shape, dtype, seed=0, device="cpu"):
+    """An upstream gradient dO of ``shape``: N(0, 1) float32 from its own
+    generator seeded with ``seed``, rounded to ``dtype`` ("f16", "bf16")."""
+    gen_device = "cpu" if str(device) == "cpu" else device
+    g = torch.Generator(device=gen_device)
+    g.manual_seed(seed)
+    x = torch.randn(tuple(shape), generator=g, dtype=torch.float32, device=gen_device)
+    return x.to(device=device, dtype=DTYPES[dtype])
+
+
 @dataclasses.dataclass(frozen=True)
 class SoftmaxWorkload:
     """A wide-row softmax input: x ~ 3 * N(0, 1) float32, rounded to dtype."""

@@ -226,3 +226,50 @@ def test_attn_fwd_gqa_rejects_bad_group(attn, hkv):
                                  None, None, None)
     assert rc == 1, _lib.lib().attn_last_error()
     assert b"Hkv" in _lib.lib().attn_last_error()
+
+
+def _bwd(attn, **kw):
+    from online_softmax_streaming_amd import _lib
+    g = 1 << 24  # fake, disjoint device addresses: every case fails before any device call
+    a = dict(q=1 * g, k=2 * g, v=3 * g, o=4 * g, do=5 * g, m=6 * g, l=7 * g, dq=8 * g, dk=9 * g,
+             dv=10 * g, b=1, h=2, hkv=2, nq=64, nk=64, d=64, causal=0, scale=0.125, dtype=2)
+    a.update(kw)
+    return _lib.lib().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["m"], a["l"], a["dq"],
+                               a["dk"], a["dv"], a["b"], a["h"], a["hkv"], a["nq"], a["nk"],
+                               a["d"], a["causal"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), 2),                       # FP32 backward is not built
+    (dict(dtype=7), 1),
+    (dict(causal=2), 1),
+    (dict(hkv=3), 1),
+    (dict(hkv=0), 1),
+    (dict(d=48), 2),
+    (dict(scale=0.0), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(nq=-1), 1),
+    (dict(q=0), 1),
+    (dict(o=0), 1),
+    (dict(do=0), 1),
+    (dict(m=0), 1),
+    (dict(dq=0), 1),
+    (dict(dk=0), 1),
+    (dict(v=0), 1),
+    (dict(q=(1 << 24) + 8), 1),               # misaligned
+    (dict(m=6 * (1 << 24) + 2), 1),           # misaligned row state
+    (dict(dq=(1 << 24) + 1024), 1),           # dQ overlaps Q
+    (dict(dk=10 * (1 << 24)), 1),             # dK is dV
+    (dict(dv=6 * (1 << 24)), 1),              # dV overlaps m
+    (dict(nq=1, b=1 << 16, h=1 << 8, hkv=1 << 8, nk=1 << 8), 1),  # B*Hkv*Nk reaches 2^32
+    (dict(nk=(1 << 31) // 64), 1),            # Nk*D reaches 2^31
+])
+def test_attn_bwd_rejects_bad_arguments(attn, kw, code):
+    from online_softmax_streaming_amd import _lib
+    assert _bwd(attn, **kw) == code, _lib.lib().attn_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(b=0), dict(h=0), dict(nq=0, nk=0),
+                                dict(b=0, q=0, k=0, v=0, o=0, do=0, m=0, l=0, dq=0, dk=0, dv=0)])
+def test_attn_bwd_empty_is_a_noop(attn, kw):
+    assert _bwd(attn, **kw) == 0

@@ -1,0 +1,231 @@
+"""GPU parity of the attention backward (attn_bwd) against the FP64 oracle.
+
+Each case runs the forward (attn_fwd_gqa with row states) and then attn_bwd
+through the C ABI, and compares dQ, dK, dV element by element with
+oracle.attention_backward on the same inputs, upcast exactly to FP64.
+
+Tolerance, derived from the arithmetic (u = unit roundoff of the input
+type, 2^-8 for bf16 and 2^-11 for f16; s = half the smallest subnormal
+spacing, 2^-25 for f16 and 2^-134 for bf16):
+  * the kernels recompute P from the forward's (m, l), whose l sums weights
+    rounded to the input type: P is off by a relative u at most;
+  * P (for dV) and dS (for dK, dQ) are rounded to the input type as
+    matrix-core operands: relative u, or absolute s where they fall below
+    the normal range;
+  * Delta uses the forward's rounded output O, off by at most
+    3u * (P |V|) + s * (vis |V|) per feature (vis = the visibility mask);
+so, per visible pair, |dS error| <= 2u P |dP - Delta| + P * (Delta error) + s,
+and |P error| <= 2u P + s.  Summing with absolute values gives per-element
+bounds b_dV = (2u P + s vis)^T |dO|, b_dK = scale * E^T |Q|,
+b_dQ = scale * E |K| (E = the dS error bound), summed over the query heads
+of a group for grouped K/V.  The check is
+    |got - ref| <= 2 b + u |ref| + a
+where u |ref| is the output cast, the factor 2 covers the FP32 rounding the
+derivation leaves out (2^-24 per term), and a is 2^-25 for f16 or 1e-37
+for bf16.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from online_softmax_streaming_amd.workloads import WORKLOADS, make_qkv, random_dout, random_qkv
+
+pytestmark = pytest.mark.gpu
+
+U = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+SUB = {"bf16": 2.0 ** -134, "f16": 2.0 ** -25}
+A = {"bf16": 1e-37, "f16": 2.0 ** -25}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import online_softmax_streaming_amd as m
+    return m
+
+
+def _inputs(b, h, hkv, nq, nk, d, dtype, seed, q_mult=1.0, k_ramp=0.0):
+    q, _, _ = random_qkv(b, h, nq, nk, d, dtype, seed=seed, device="cuda")
+    _, k, v = random_qkv(b, hkv, nq, nk, d, dtype, seed=seed + 1, device="cuda", k_ramp=k_ramp)
+    if q_mult != 1.0:
+        q = (q.float() * q_mult).to(q.dtype)
+    do = random_dout((b, h, nq, d), dtype, seed=seed + 2, device="cuda")
+    return q, k, v, do
+
+
+def _run(lib, q, k, v, do, causal):
+    out, m, l = lib.attn_fwd_gqa(q, k, v, causal=causal, want_stats=True)
+    dq, dk, dv = lib.attn_bwd(q, k, v, out, do, m, l, causal=causal)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _head_bounds(q, k, v, do, causal, scale, dtype):
+    """Error bounds (dQ, dK, dV) of one head; see the module docstring."""
+    u, sub = U[dtype], SUB[dtype]
+    p = oracle.probabilities(q, k, causal, scale)
+    vis = (p > 0).astype(np.float64)
+    dp = do @ v.T
+    delta = (do * (p @ v)).sum(axis=1)
+    err_delta = (np.abs(do) * (3 * u * (p @ np.abs(v)) + sub * (vis @ np.abs(v)))).sum(axis=1)
+    err_ds = 2 * u * p * np.abs(dp - delta[:, None]) + p * err_delta[:, None] + sub * vis
+    return (scale * (err_ds @ np.abs(k)), scale * (err_ds.T @ np.abs(q)),
+            (2 * u * p + sub * vis).T @ np.abs(do))
+
+
+def _check(lib, q, k, v, do, causal, got, heads=None):
+    """Compare got = (dq, dk, dv) with the oracle; ``heads`` limits the
+    check to some (b, kv-head) pairs (all when None)."""
+    dtype = {torch.bfloat16: "bf16", torch.float16: "f16"}[q.dtype]
+    d = q.shape[-1]
+    scale = lib.default_scale(d)
+    g = q.shape[1] // k.shape[1]
+    qd, kd, vd, dod = (t.cpu().double().numpy() for t in (q, k, v, do))
+    gq, gk, gv = (t.cpu().double().numpy() for t in got)
+    if heads is None:
+        heads = [(b, hk) for b in range(q.shape[0]) for hk in range(k.shape[1])]
+    for b, hk in heads:
+        want_dk = np.zeros_like(kd[b, hk])
+        want_dv = np.zeros_like(vd[b, hk])
+        bnd_dk = np.zeros_like(want_dk)
+        bnd_dv = np.zeros_like(want_dv)
+        for h in range(hk * g, hk * g + g):
+            args = (qd[b, h], kd[b, hk], vd[b, hk], dod[b, h], causal, scale)
+            wq, wk, wv = oracle.attention_backward_head(*args)
+            mq, mk, mv = _head_bounds(*args, dtype)
+            want_dk += wk
+            want_dv += wv
+            bnd_dk += mk
+            bnd_dv += mv
+            _assert_close(gq[b, h], wq, mq, dtype, f"dQ[{b},{h}]")
+        _assert_close(gk[b, hk], want_dk, bnd_dk, dtype, f"dK[{b},{hk}]")
+        _assert_close(gv[b, hk], want_dv, bnd_dv, dtype, f"dV[{b},{hk}]")
+
+
+def _bound(b, want, dtype):
+    return 2 * b + U[dtype] * np.abs(want) + A[dtype]
+
+
+def _assert_close(got, want, b, dtype, what):
+    assert np.all(np.isfinite(got)), what
+    bound = _bound(b, want, dtype)
+    excess = np.abs(got - want) - bound
+    worst = float(excess.max()) if excess.size else 0.0
+    assert worst <= 0.0, (f"{what}: max excess {worst:.3g}, max abs err "
+                          f"{np.abs(got - want).max():.3g}, max |ref| {np.abs(want).max():.3g}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("b,h,nq,nk,d", [
+    (1, 2, 200, 200, 128),
+    (2, 2, 77, 133, 64),
+    (2, 1, 130, 61, 32),    # causal: the first 69 rows see no key
+    (1, 2, 1, 1, 16),
+    (1, 1, 64, 64, 128),
+    (1, 2, 300, 300, 64),
+    (1, 1, 257, 513, 128),  # two query tiles of the dQ kernel, five key blocks of dK/dV
+    (1, 1, 700, 700, 16),
+    (1, 1, 5, 700, 128),
+])
+def test_parity(lib, dtype, causal, b, h, nq, nk, d):
+    q, k, v, do = _inputs(b, h, h, nq, nk, d, dtype, seed=nq * 31 + nk + d)
+    got = _run(lib, q, k, v, do, causal)
+    _check(lib, q, k, v, do, causal, got)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("h,hkv,nq,nk,d", [(8, 2, 259, 517, 128), (4, 1, 300, 300, 64),
+                                           (6, 3, 130, 70, 32)])
+def test_grouped_kv(lib, causal, h, hkv, nq, nk, d):
+    q, k, v, do = _inputs(2, h, hkv, nq, nk, d, "bf16", seed=h + hkv + nq)
+    got = _run(lib, q, k, v, do, causal)
+    _check(lib, q, k, v, do, causal, got)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_large_logits_and_rising_keys(lib, dtype):
+    # Scores spread over tens of units and a key ramp: P spans many orders
+    # of magnitude and the lse must come from the forward's exact row max.
+    q, k, v, do = _inputs(1, 2, 2, 333, 333, 64, dtype, seed=5, q_mult=5.0, k_ramp=0.02)
+    got = _run(lib, q, k, v, do, True)
+    _check(lib, q, k, v, do, True, got)
+
+
+def test_rows_without_keys_get_zero_dq(lib):
+    q, k, v, do = _inputs(1, 2, 2, 200, 50, 64, "bf16", seed=8)
+    dq, dk, dv = _run(lib, q, k, v, do, True)
+    assert torch.count_nonzero(dq[:, :, :150]).item() == 0
+
+
+def test_no_queries_gives_zero_dk_dv(lib):
+    q, k, v, do = _inputs(1, 2, 2, 0, 100, 64, "bf16", seed=9)
+    out = torch.empty_like(q)
+    m = torch.empty((1, 2, 0), dtype=torch.float32, device="cuda")
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(v, 7.0)
+    lib.attn_bwd(q, k, v, out, do, m, m.clone(), dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dk).item() == 0 and torch.count_nonzero(dv).item() == 0
+
+
+def test_no_keys_gives_zero_dq(lib):
+    q, k, v, do = _inputs(1, 2, 2, 100, 0, 64, "bf16", seed=10)
+    out, m, l = lib.attn_fwd_gqa(q, k, v, want_stats=True)
+    dq = torch.full_like(q, 7.0)
+    lib.attn_bwd(q, k, v, out, do, m, l, dq=dq)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dq).item() == 0
+
+
+def test_bitwise_reproducible(lib):
+    q, k, v, do = _inputs(2, 4, 2, 517, 517, 128, "bf16", seed=11)
+    a = _run(lib, q, k, v, do, True)
+    b = _run(lib, q, k, v, do, True)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_side_stream(lib):
+    q, k, v, do = _inputs(1, 2, 2, 300, 300, 64, "bf16", seed=12)
+    out, m, l = lib.attn_fwd_gqa(q, k, v, causal=True, want_stats=True)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got = lib.attn_bwd(q, k, v, out, do, m, l, causal=True, stream=s)
+    s.synchronize()
+    _check(lib, q, k, v, do, True, got)
+
+
+def test_tolerance_rejects_planted_mistakes(lib):
+    # The bound must be tight enough to catch plausible kernel mistakes.  Each
+    # is planted in the oracle on the CPU; the GPU result must then fail the
+    # bound against the planted version.
+    q, k, v, do = _inputs(1, 1, 1, 200, 200, 64, "bf16", seed=13)
+    got = _run(lib, q, k, v, do, True)
+    scale = lib.default_scale(64)
+    qd, kd, vd, dod = (t.cpu().double().numpy()[0, 0] for t in (q, k, v, do))
+    gq, gk, gv = (t.cpu().double().numpy()[0, 0] for t in got)
+    mq, mk, mv = _head_bounds(qd, kd, vd, dod, True, scale, "bf16")
+    p = oracle.probabilities(qd, kd, True, scale)
+    ds_bad = oracle.softmax_vjp(p, dod @ vd.T, bugs=("unweighted_reduction",))
+    ds = oracle.softmax_vjp(p, dod @ vd.T)
+    p_nodiag = oracle.probabilities(qd, kd, True, scale) * (1 - np.eye(200))
+    planted = {
+        "unweighted reduction (dQ)": (gq, scale * ds_bad @ kd, mq),
+        "dropped scale (dK)": (gk, ds.T @ qd, mk),
+        "diagonal masked (dV)": (gv, p_nodiag.T @ dod, mv),
+    }
+    for name, (g, bad, b) in planted.items():
+        assert np.any(np.abs(g - bad) > _bound(b, bad, "bf16")), name
+
+
+@pytest.mark.parametrize("name", ["headline_causal_bf16", "headline_noncausal_bf16"])
+def test_headline_sampled_heads(lib, name):
+    # The benchmark's workload at full size, in the launch configuration the
+    # benchmark times; two whole heads are checked against the oracle.
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w, seed=0, device="cuda")
+    do = random_dout(q.shape, w.dtype, seed=1, device="cuda")
+    got = _run(lib, q, k, v, do, w.causal)
+    _check(lib, q, k, v, do, w.causal, got, heads=[(0, 0), (w.B - 1, w.H - 1)])

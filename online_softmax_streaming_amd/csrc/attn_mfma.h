@@ -13,6 +13,8 @@
 // M[r][0..3], lane i receives M[4e + i/4][i%4] for e = 0..3.
 #pragma once
 
+#include <type_traits>
+
 #include "attn_device.h"
 
 namespace attn {
@@ -85,6 +87,17 @@ __device__ __forceinline__ float half_max(float x) {
 __device__ __forceinline__ float half_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Calls f(std::integral_constant<int, i>) for i = B .. E-1 in order: a loop
+// whose index is a compile-time constant in the body, so register arrays it
+// indexes stay in registers whatever the unroller decides.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 }  // namespace attn

@@ -89,6 +89,10 @@ constexpr int kBT = 64;  // rows of every streamed tile (keys in dq, queries in 
 constexpr int kPF = ATTN_BWD_PF;    // row-fragment reads in flight ahead of their MFMA
 constexpr int kTPF = ATTN_BWD_TPF;  // transpose reads in flight ahead of their MFMA
 constexpr float kPosInf = __builtin_inff();
+#ifndef ATTN_BWD_STAGE_STRIDE
+#define ATTN_BWD_STAGE_STRIDE 2
+#endif
+constexpr int kStageStride = ATTN_BWD_STAGE_STRIDE;  // MFMAs between two staging loads (dK/dV)
 
 // XCD-aware workgroup order (consecutive ids go round-robin over the 8
 // XCDs): each XCD walks a contiguous range of logical workgroups, so the
@@ -121,6 +125,13 @@ __device__ __forceinline__ void transpose_offsets(int lane, int (&off)[NB][2]) {
     }
   }
 }
+
+// Buffer resources of one staged (query head, tile) pair of the dK/dV
+// kernel: Q rows, dO rows and (lse2, Delta) rows, and the tile's first row.
+struct StageSource {
+  __amdgpu_buffer_rsrc_t q, g, st;
+  int q0;
+};
 
 template <typename T>
 __device__ __forceinline__ typename Mfma<T>::vec8 transpose_read(const unsigned char* tile, int o0,
@@ -399,7 +410,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NB = DP / 32;
   constexpr int NT = NW * 64;
   constexpr int TILE = BQ * D * 2;
-  constexpr int STAT = 1024;  // (lse2, Delta) of 128 rows; the tile uses the first 64
+  constexpr int STAT = 1024 * NW;  // per wave: (lse2, Delta) of 128 rows, the tile uses 64
   static_assert(G::steps_keep_swizzle(), "tile steps must keep the LDS swizzle");
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem0[2][TILE];  // [Q, dO]
@@ -463,122 +474,193 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int n = 0; n < NB; ++n) adv[n] = adk[n] = f32x16{};
 
-    auto stage = [&](int it, int buf) __attribute__((always_inline)) {
+    // Staging of (query head, tile) pair `it` into one LDS buffer, one load
+    // instruction at a time, so the loads can be spread between the MFMAs of
+    // the tile being computed: part u < NPT moves this thread's u-th 16-byte
+    // slot of the Q tile, NPT <= u < 2*NPT of the dO tile, and part 2*NPT
+    // the tile's (lse2, Delta) rows into the wave's own 1 KB copy, lane l
+    // holding rows 2l, 2l+1 (a copy per wave keeps the staging free of
+    // branches).  Rows past Nq are out of the buffer range and read as zero.
+    constexpr int NSLOT = BQ * D * 2 / 16;
+    constexpr int NPT = (NSLOT + NT - 1) / NT;
+    constexpr int NPART = 2 * NPT + 1;
+    static_assert(NSLOT % 64 == 0, "a wave moves whole 1 KB LDS blocks");
+    auto source = [&](int it) __attribute__((always_inline)) -> StageSource {
       const int g = it / nt;
       const int q0 = (t0 + it - g * nt) * BQ;
       const int64_t bh = (int64_t)bhkv * a.group + g;
-      const T* Qh = static_cast<const T*>(a.q) + bh * Nq * D;
-      const T* dOh = static_cast<const T*>(a.dout) + bh * Nq * D;
-      stage_pair<T, D, NT>(Qh, dOh, Nq, q0, tile_ptr(buf, 0), tile_ptr(buf, 1), tid, wave);
-      if (wave == 0) {
-        // Rows q0 + 2l, q0 + 2l + 1 of (lse2, Delta) for lane l; rows past
-        // Nq read as zero.
-        const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-            a.stat + 2 * bh * Nq, 0, (int)((uint32_t)Nq * 8u), 0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, LDS_PTR(void, stat_ptr(buf)), 16,
-                                                 (int)((uint32_t)q0 * 8u + (uint32_t)lane * 16u),
-                                                 0, 0, 0);
+      const uint32_t bytes = (uint32_t)Nq * (uint32_t)(2 * D);
+      StageSource src;
+      src.q = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<T*>(static_cast<const T*>(a.q) + bh * Nq * D), 0, (int)bytes, 0x00020000);
+      src.g = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<T*>(static_cast<const T*>(a.dout) + bh * Nq * D), 0, (int)bytes, 0x00020000);
+      src.st = __builtin_amdgcn_make_buffer_rsrc(a.stat + 2 * bh * Nq, 0,
+                                                 (int)((uint32_t)Nq * 8u), 0x00020000);
+      src.q0 = q0;
+      return src;
+    };
+    auto stage_part = [&](const StageSource& src, int buf, int u) __attribute__((always_inline)) {
+      if (u < 2 * NPT) {
+        const int uu = u % NPT;
+        const int sl = tid + uu * NT;
+        const int sl0 = wave * 64 + uu * NT;
+        if (NSLOT % NT == 0 || sl0 < NSLOT) {
+          const int row = sl / G::CPR;
+          const int chunk = (sl % G::CPR) ^ G::swz(row);
+          const int j = min(src.q0 + row, Nq);
+          const uint32_t vo = (uint32_t)j * (uint32_t)(2 * D) + (uint32_t)(chunk << 4);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(u < NPT ? src.q : src.g,
+                                                   LDS_PTR(void, tile_ptr(buf, u < NPT ? 0 : 1) + sl0 * 16),
+                                                   16, (int)vo, 0, 0, 0);
+        }
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            src.st, LDS_PTR(void, stat_ptr(buf) + wave * 1024), 16,
+            (int)((uint32_t)src.q0 * 8u + (uint32_t)lane * 16u), 0, 0, 0);
       }
     };
 
-    auto compute = [&](auto bufc, int q0, bool need_mask) {
+    // One tile in four phases over its two 32-query blocks, so the softmax
+    // gradient of one block runs on the VALU while the matrix cores work on
+    // the other (one wave per SIMD: nothing else would fill the gaps):
+    //   1: S, dP of block 0
+    //   2: S, dP of block 1     + P, dS of block 0
+    //   3: dV, dK of block 0    + P, dS of block 1
+    //   4: dV, dK of block 1
+    // Every MFMA operand read from LDS is issued kPF MFMAs ahead of its use,
+    // across phase boundaries, and the loads of the next tile into the other
+    // buffer are spread evenly between the MFMAs.
+    auto compute = [&](auto bufc, int q0, bool need_mask, const StageSource& nsrc) {
       constexpr int buf = decltype(bufc)::value;
       const unsigned char* qt = tile_ptr(buf, 0);
       const unsigned char* gt = tile_ptr(buf, 1);
-      const float* st = reinterpret_cast<const float*>(stat_ptr(buf));
+      const float* st = reinterpret_cast<const float*>(stat_ptr(buf) + wave * 1024);
+      static_assert(BQ == 64, "two 32-query blocks per tile");
+      // Causal mask: key krow is hidden from the query of register r of
+      // block mb iff 32mb + 8(r/4) + r%4 < kq (the lane's 4*h32 row offset is
+      // folded into kq, so each test compares an immediate); kq is below
+      // every row when the tile needs no mask (a select, not a branch).
+      const int kq = need_mask ? krow - q0 - off - 4 * h32 : -(1 << 30);
+      constexpr int NF = 2 * KC;  // S and dP MFMAs of one block
+      constexpr int NG = 4 * NB;  // dV and dK MFMAs of one block
+      constexpr int NSTEP = 2 * NF + 2 * NG;
+      // Staging loads go out early (one every kStageStride MFMAs from the
+      // start) so they have landed by the barrier that ends the tile.
+      constexpr int SSTRIDE = NSTEP / NPART < kStageStride ? NSTEP / NPART : kStageStride;
+      static_assert(SSTRIDE >= 1, "one staging load per MFMA at most");
 
-      // S = Q K^T (MFMAs 0..NS-1) and dP = dO V^T (NS..2NS-1): operand i is
-      // query block (i % NS) / KC, feature chunk i % KC of the Q or dO tile.
-      constexpr int NS = (BQ / 32) * KC;
-      auto fread = [&](int i) {
-        const unsigned char* t = i < NS ? qt : gt;
-        const int ii = i < NS ? i : i - NS;
-        return *reinterpret_cast<const vec8*>(t + qoff[ii % KC] + (ii / KC) * 32 * 2 * D);
-      };
-      vec8 ff[2 * NS];
-#pragma unroll
-      for (int i = 0; i < kPF && i < 2 * NS; ++i) ff[i] = fread(i);
-      f32x16 s[BQ / 32], dp[BQ / 32];
-#pragma unroll
-      for (int mb = 0; mb < BQ / 32; ++mb) s[mb] = dp[mb] = f32x16{};
-#pragma unroll
-      for (int i = 0; i < 2 * NS; ++i) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (i + kPF < 2 * NS) ff[i + kPF] = fread(i + kPF);
-        if (i < NS)
-          s[i / KC] = Mfma<T>::mma(ff[i], kf[i % KC], s[i / KC]);
-        else
-          dp[(i - NS) / KC] = Mfma<T>::mma(ff[i], vf[(i - NS) % KC], dp[(i - NS) / KC]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-
-      // dO^T and Q^T operands (MFMAs 0..NV-1 update dV, NV..2NV-1 dK):
-      // feature block (i % NV) / (BQ/16), query group i % (BQ/16).
-      constexpr int NV = NB * (BQ / 16);
-      auto tread = [&](int i) {
-        const unsigned char* t = i < NV ? gt : qt;
-        const int ii = i < NV ? i : i - NV;
-        const int n = ii / (BQ / 16), c2 = ii % (BQ / 16);
-        return transpose_read<T>(t, toff[n][0] + 16 * c2 * 2 * D, toff[n][1] + 16 * c2 * 2 * D);
-      };
-      vec8 tf[2 * NV];
-#pragma unroll
-      for (int i = 0; i < kTPF && i < 2 * NV; ++i) tf[i] = tread(i);
-      __builtin_amdgcn_sched_barrier(0);
-
-      // Row r of C-layout block mb is query q0 + 32mb + 8(r/4) + 4*h32 + r%4;
-      // its (lse2, Delta) pairs for r%4 = 0..3 are 32 contiguous bytes.
-      vec8 pf[BQ / 16], dsf[BQ / 16];
-#pragma unroll
-      for (int mb = 0; mb < BQ / 32; ++mb) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int qr = 32 * mb + 8 * g4 + 4 * h32;
-          const f32x4 s0 = *reinterpret_cast<const f32x4*>(st + 2 * qr);
-          const f32x4 s1 = *reinterpret_cast<const f32x4*>(st + 2 * qr + 4);
-          const float l2[4] = {s0[0], s0[2], s1[0], s1[2]};
-          const float dl[4] = {s0[1], s0[3], s1[1], s1[3]};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g4 + e;
-            float x = s[mb][r];
-            if (need_mask && krow > q0 + qr + e + off) x = kNegInf;
-            const float p = exp2_hw(__builtin_fmaf(x, c, -l2[e]));
-            const int c2 = 2 * mb + (r >> 3);
-            pf[c2][r & 7] = from_f32<T>(p);
-            dsf[c2][r & 7] = from_f32<T>(p * (dp[mb][r] - dl[e]));
-          }
+      // Operand of MFMA k, in issue order.  S/dP steps: Q (i < KC) or dO
+      // fragment, query block mb.  dV/dK steps: dO^T (i < 2NB) or Q^T,
+      // feature block n = (i % 2NB) / 2, 16-query group 2mb + i % 2.
+      auto read_op = [&](auto kk) __attribute__((always_inline)) -> vec8 {
+        constexpr int k = decltype(kk)::value;
+        if constexpr (k < 2 * NF) {
+          constexpr int mb = k / NF, i = k % NF;
+          const unsigned char* t = i < KC ? qt : gt;
+          return *reinterpret_cast<const vec8*>(t + qoff[i % KC] + mb * 32 * 2 * D);
+        } else {
+          constexpr int mb = (k - 2 * NF) / NG, i = (k - 2 * NF) % NG;
+          constexpr int ii = i % (2 * NB);
+          constexpr int c2 = 2 * mb + (ii & 1), n = ii >> 1;
+          const unsigned char* t = i < 2 * NB ? gt : qt;
+          return transpose_read<T>(t, toff[n][0] + 16 * c2 * 2 * D, toff[n][1] + 16 * c2 * 2 * D);
         }
-      }
+      };
 
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 2 * NV; ++i) {
+      f32x16 s[2], dp[2];
+      vec8 pf[2][2], dsf[2][2];  // [block][16-query group]
+      vec8 op[NSTEP];
+      f32x4 sv[2][4][2];  // (lse2, Delta) of 4 rows: [block][row group][pair of rows]
+
+      auto mma_step = [&](auto kk) __attribute__((always_inline)) {
+        constexpr int k = decltype(kk)::value;
+        if constexpr (k < 2 * NF) {
+          constexpr int mb = k / NF, i = k % NF;
+          if constexpr (i < KC) s[mb] = Mfma<T>::mma(op[k], kf[i], s[mb]);
+          else dp[mb] = Mfma<T>::mma(op[k], vf[i - KC], dp[mb]);
+        } else {
+          constexpr int mb = (k - 2 * NF) / NG, i = (k - 2 * NF) % NG;
+          constexpr int ii = i % (2 * NB), n = ii >> 1, cc = ii & 1;
+          if constexpr (i < 2 * NB) adv[n] = Mfma<T>::mma(op[k], pf[mb][cc], adv[n]);
+          else adk[n] = Mfma<T>::mma(op[k], dsf[mb][cc], adk[n]);
+        }
+      };
+      // Rows 32mb + 8g4 + 4*h32 + 0..3: the rows of registers 4g4..4g4+3.
+      auto read_stats = [&](int mb, int g4) __attribute__((always_inline)) {
+        const int qr = 32 * mb + 8 * g4 + 4 * h32;
+        sv[mb][g4][0] = *reinterpret_cast<const f32x4*>(st + 2 * qr);
+        sv[mb][g4][1] = *reinterpret_cast<const f32x4*>(st + 2 * qr + 4);
+      };
+      auto grad = [&](auto mbc, auto rc) __attribute__((always_inline)) {
+        constexpr int mb = decltype(mbc)::value, r = decltype(rc)::value;
+        // The next row group's statistics are requested one group ahead.
+        if constexpr ((r & 3) == 0) {
+          if constexpr (r < 12) read_stats(mb, (r >> 2) + 1);
+          else if constexpr (mb == 0) read_stats(1, 0);
+        }
+        const f32x4 pr = sv[mb][r >> 2][(r >> 1) & 1];
+        const float l2 = pr[2 * (r & 1)], dl = pr[2 * (r & 1) + 1];
+        float x = s[mb][r];
+        if (32 * mb + 8 * (r >> 2) + (r & 3) < kq) x = kNegInf;
+        const float p = exp2_hw(__builtin_fmaf(x, c, -l2));
+        pf[mb][r >> 3][r & 7] = from_f32<T>(p);
+        dsf[mb][r >> 3][r & 7] = from_f32<T>(p * (dp[mb][r] - dl));
+      };
+
+      s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+      static_for<0, (kPF < NSTEP ? kPF : NSTEP)>([&](auto kk) { op[decltype(kk)::value] = read_op(kk); });
+      read_stats(0, 0);
+      static_for<0, NSTEP>([&](auto kk) {
+        constexpr int k = decltype(kk)::value;
         __builtin_amdgcn_sched_barrier(0);
-        if (i + kTPF < 2 * NV) tf[i + kTPF] = tread(i + kTPF);
-        if (i < NV)
-          adv[i / (BQ / 16)] = Mfma<T>::mma(tf[i], pf[i % (BQ / 16)], adv[i / (BQ / 16)]);
-        else
-          adk[(i - NV) / (BQ / 16)] =
-              Mfma<T>::mma(tf[i], dsf[(i - NV) % (BQ / 16)], adk[(i - NV) / (BQ / 16)]);
-      }
+        if constexpr (k + kPF < NSTEP)
+          op[k + kPF] = read_op(std::integral_constant<int, k + kPF>{});
+        mma_step(kk);
+        if constexpr (k % SSTRIDE == SSTRIDE - 1 && k / SSTRIDE < NPART)
+          stage_part(nsrc, buf ^ 1, k / SSTRIDE);
+        // Phase 2 (k in [NF, 2NF)) grads block 0, phase 3 block 1; the 16
+        // registers are spread evenly over the phase's MFMAs.
+        if constexpr (k >= NF && k < 2 * NF) {
+          constexpr int j = k - NF;
+          static_for<16 * j / NF, 16 * (j + 1) / NF>(
+              [&](auto rc) { grad(std::integral_constant<int, 0>{}, rc); });
+        } else if constexpr (k >= 2 * NF && k < 2 * NF + NG) {
+          constexpr int j = k - 2 * NF;
+          static_for<16 * j / NG, 16 * (j + 1) / NG>(
+              [&](auto rc) { grad(std::integral_constant<int, 1>{}, rc); });
+        }
+      });
       __builtin_amdgcn_sched_barrier(0);
     };
 
     if (nit > 0) {
-      stage(0, 0);
+      {
+        const StageSource s0 = source(0);
+#pragma unroll
+        for (int u = 0; u < NPART; ++u) stage_part(s0, 0, u);
+      }
       __syncthreads();
       auto step = [&](auto bufc, int it) {
         constexpr int buf = decltype(bufc)::value;
         const int g = it / nt;
         const int q0 = (t0 + it - g * nt) * BQ;
-        if (it + 1 < nit) stage(it + 1, buf ^ 1);
-        // The tile's last query sees this wave's first key: some work.
-        const bool active = kw0 < Nk && (!CAUSAL || kw0 <= q0 + BQ - 1 + off);
-        if (active) {
+        // After the last pair the loads fetch the current tile again into
+        // the idle buffer, which nothing reads: staging stays branch-free.
+        const StageSource nsrc = source(it + 1 < nit ? it + 1 : it);
+        // A causal wave whose keys no query of this tile sees (only on a
+        // pass's first tile) still runs the tile with every score masked:
+        // P = dS = 0 adds nothing, it would wait at the barrier anyway, and
+        // a data-dependent branch here costs the loop ~100 registers.
+        if (kw0 < Nk) {
           const bool need_mask = CAUSAL && kw0 + 31 > q0 + off;
-          compute(bufc, q0, need_mask);
+          compute(bufc, q0, need_mask, nsrc);
+        } else {
+#pragma unroll
+          for (int u = 0; u < NPART; ++u) stage_part(nsrc, buf ^ 1, u);
         }
+        // Buffer buf^1 was last read in step it-1, before that step's
+        // barrier; this barrier also waits for the loads into it.
         __syncthreads();
       };
       for (int it = 0; it < nit; it += 2) {

@@ -51,6 +51,12 @@ class Workload:
         """Algorithmic FLOP: 2*D for Q.K^T plus 2*D for P.V per visible pair."""
         return 4 * self.D * self.visible_pairs()
 
+    def bwd_flops(self):
+        """Algorithmic FLOP of the backward: 2*D for each of the five products
+        per visible pair (Q.K^T recomputed, dO.V^T, P^T dO, dS^T Q, dS K),
+        2.5 times the forward's count."""
+        return 10 * self.D * self.visible_pairs()
+
     def bytes(self):
         """Algorithmic HBM bytes: Q, K, V read once and out written once."""
         el = torch.finfo(self.torch_dtype).bits // 8

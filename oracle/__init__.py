@@ -39,6 +39,7 @@ from .softmax import (  # noqa: F401
     softmax_rows,
     split_softmax_model,
 )
+from .paged import attention_paged, gather_pages  # noqa: F401
 from .attention_backward import (  # noqa: F401
     attention_backward,
     attention_backward_head,

@@ -46,24 +46,34 @@ EMPTY_STATE = (NEG_INF, 0.0)
 _ROW_CHUNK_ELEMS = 1 << 24  # fp64 score elements materialised per chunk
 
 
-def visible_mask(nq, nk, causal, rows=None):
+def visible_mask(nq, nk, causal, rows=None, window=0):
     """Boolean [len(rows), nk]: True where key j is visible to query row i.
 
     Workshops page, "Scope and contracts": causal attention includes the
     diagonal (j <= i for Nq == Nk).  For Nq != Nk the keys are aligned to the
     end of the query block (j <= i + Nk - Nq), which reduces to the pages'
     rule when the two lengths agree.
+
+    ``window`` > 0 (causal only) keeps the ``window`` keys that end at the
+    row's diagonal: j > i + (Nk - Nq) - window.  The pages name sliding
+    windows only as planned work; this is the usual reading.
     """
     if rows is None:
         rows = np.arange(nq)
     rows = np.asarray(rows, dtype=np.int64)
     j = np.arange(nk, dtype=np.int64)[None, :]
+    if window and not causal:
+        raise ValueError("a sliding window needs causal attention")
     if not causal:
         return np.ones((rows.shape[0], nk), dtype=bool)
-    return j <= rows[:, None] + (nk - nq)
+    diag = rows[:, None] + (nk - nq)
+    vis = j <= diag
+    if window:
+        vis &= j > diag - window
+    return vis
 
 
-def attention_rows(q, k, v, causal, scale, rows=None):
+def attention_rows(q, k, v, causal, scale, rows=None, window=0):
     """Two-pass FP64 attention for one head, on the query rows ``rows``.
 
     q: [Nq, D], k: [Nk, D], v: [Nk, Dv] arrays (upcast exactly to float64 by
@@ -71,7 +81,7 @@ def attention_rows(q, k, v, causal, scale, rows=None):
 
     Returns (out [R, Dv], m [R], l [R]) where (m, l) is the row's merge state
     in natural-log units: sum_j exp(s_j) = l * exp(m); (m, l) = (-inf, 0) and
-    out = 0 for a row with no visible key.
+    out = 0 for a row with no visible key.  ``window`` as in visible_mask.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -93,7 +103,7 @@ def attention_rows(q, k, v, causal, scale, rows=None):
         r = rows[c0:c0 + step]
         # Scores for these rows, materialised in FP64.
         s = scale * (q[r] @ k.T)
-        vis = visible_mask(nq, nk, causal, r)
+        vis = visible_mask(nq, nk, causal, r, window)
         s = np.where(vis, s, NEG_INF)
         nonempty = vis.any(axis=1)
 

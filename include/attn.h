@@ -175,6 +175,52 @@ ATTN_API int attn_bwd(const void* Q, const void* K, const void* V, const void* O
                       int64_t D, int causal, float scale, int dtype, void* stream);
 
 /*
+ * attn_decode_paged -- attention of a few query rows per head over a paged
+ * key/value cache, with an optional sliding window (a KV-cache slice and a
+ * sliding window: the decode variants the workshops page plans for a later
+ * week; the computation per row is attn_fwd_gqa's, [AK] row A3).
+ *
+ * Sequence b has seq_lens[b] keys (clamped to [0, max_pages * page_size]);
+ * its key j lives in physical page block_table[b * max_pages + j / page_size]
+ * at row j % page_size.  Query head h of sequence b attends with K/V head
+ * h / (H / Hkv).  Visibility for query row i, with off = seq_lens[b] - Nq:
+ * every key when causal == 0; keys j <= i + off when causal == 1; and with
+ * window > 0 (causal == 1 only) also j > i + off - window, i.e. the `window`
+ * keys ending at the row's diagonal.  A row with no visible key gets out = 0
+ * and (m, l) = (-inf, 0).  Keys are split across workgroups and the partial
+ * states folded with the A1 merge ([AK] rows A1, A2), as attn_fwd does for
+ * Nq <= 8; any Nq >= 1 is accepted.
+ *
+ * Layout: Q and out contiguous [B, H, Nq, D]; K_cache and V_cache contiguous
+ * [num_pages, Hkv, page_size, D] (one page of one head is contiguous);
+ * block_table int32 [B, max_pages]; seq_lens int32 [B]; m_out, l_out
+ * optional FP32 [B, H, Nq] as in attn_fwd_stats.  dtype as attn_fwd (FP32
+ * accumulation; out written with one round-to-nearest-even cast).
+ *
+ * Arguments:
+ *   Q, K_cache, V_cache, out  device pointers, 16-byte aligned; out must not
+ *            overlap an input.
+ *   block_table, seq_lens     device int32 arrays, 4-byte aligned.  Their
+ *            values are not scanned: a table entry outside [0, num_pages) is
+ *            read as an absent key (it contributes nothing); entries past a
+ *            sequence's length are never read.
+ *   page_size a power of two in [1, 2^20]; num_pages >= 1, max_pages >= 1,
+ *            max_pages * page_size < 2^31, B * H * Nq < 2^31.
+ *   causal   0 or 1; window >= 0 (0 = none; > 0 needs causal == 1).
+ *   D, scale, dtype, stream: as attn_fwd.  B, H or Nq == 0 is a no-op.
+ * Memory: partial states of the key splits in a scratch array taken with
+ * hipMallocAsync / hipFreeAsync on `stream`.
+ * Returns ATTN_OK once queued; ATTN_E_INVALID / ATTN_E_UNSUPPORTED /
+ * ATTN_E_HIP as attn_fwd.
+ */
+ATTN_API int attn_decode_paged(const void* Q, const void* K_cache, const void* V_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               void* out, int64_t B, int64_t H, int64_t Hkv, int64_t Nq,
+                               int64_t D, int64_t num_pages, int64_t page_size,
+                               int64_t max_pages, int causal, int64_t window, float scale,
+                               int dtype, float* m_out, float* l_out, void* stream);
+
+/*
  * online_merge -- merge two A1 summaries ([AK] row A1 and its worked answer).
  *
  * A state (m, l) stands for sum_j exp(x_j) = l * exp(m); (-inf, 0) is the

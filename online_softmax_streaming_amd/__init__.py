@@ -16,6 +16,7 @@ from .attn import (  # noqa: F401
     ATTN_OK,
     AttnError,
     attn_bwd,
+    attn_decode_paged,
     attn_fwd,
     attn_fwd_gqa,
     attn_fwd_raw,

@@ -30,6 +30,9 @@ SIGNATURES = {
                                     _c_ptr, _c_ptr, _c_ptr]),
     "attn_bwd": (ctypes.c_int, [_c_ptr] * 10 + [_c_i64] * 6 + [ctypes.c_int, ctypes.c_float,
                                                                  ctypes.c_int, _c_ptr]),
+    "attn_decode_paged": (ctypes.c_int, [_c_ptr] * 6 + [_c_i64] * 8 + [ctypes.c_int, _c_i64,
+                                                                       ctypes.c_float, ctypes.c_int,
+                                                                       _c_ptr, _c_ptr, _c_ptr]),
     "online_merge": (ctypes.c_int, [ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                     ctypes.c_double, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_double)]),

@@ -181,6 +181,63 @@ def attn_bwd(q, k, v, out, dout, m, l, causal=False, scale=None, dq=None, dk=Non
     return dq, dk, dv
 
 
+def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, causal=True, window=0,
+                      scale=None, out=None, m_out=None, l_out=None, want_stats=False,
+                      stream=None):
+    """Attention over a paged K/V cache; returns (out, m, l) (m, l None
+    unless ``want_stats``).
+
+    q: [B, H, Nq, D]; k_cache, v_cache: [num_pages, Hkv, page_size, D]
+    (Hkv dividing H, page_size a power of two); block_table: int32
+    [B, max_pages] of physical page indices; seq_lens: int32 [B] key counts.
+    ``window`` > 0 keeps the last ``window`` keys up to each row's diagonal
+    (needs ``causal``).
+    """
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D GPU tensor")
+        if not t.is_contiguous() or t.dtype not in _DTYPES or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be contiguous and share q's dtype")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    b, h, nq, d = q.shape
+    num_pages, hkv, page_size, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("q and the caches disagree on D")
+    for name, t in (("block_table", block_table), ("seq_lens", seq_lens)):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.device != q.device
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+    if block_table.dim() != 2 or block_table.shape[0] != b or seq_lens.shape != (b,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = default_scale(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor like q")
+    if want_stats:
+        m_out = torch.empty((b, h, nq), dtype=torch.float32, device=q.device) if m_out is None else m_out
+        l_out = torch.empty((b, h, nq), dtype=torch.float32, device=q.device) if l_out is None else l_out
+        for name, t in (("m_out", m_out), ("l_out", l_out)):
+            if (t.dtype != torch.float32 or t.device != q.device or t.shape != (b, h, nq)
+                    or not t.is_contiguous()):
+                raise ValueError(f"{name} must be a contiguous float32 [B, H, Nq] GPU tensor")
+    with torch.cuda.device(q.device):
+        sh = _stream_handle(stream, q.device)
+        stats = ((ctypes.c_void_p(m_out.data_ptr()), ctypes.c_void_p(l_out.data_ptr()))
+                 if want_stats else (None, None))
+        rc = lib().attn_decode_paged(
+            *(ctypes.c_void_p(t.data_ptr()) for t in (q, k_cache, v_cache, block_table, seq_lens,
+                                                      out)),
+            b, h, hkv, nq, d, num_pages, page_size, max_pages, int(bool(causal)), int(window),
+            float(scale), _DTYPES[q.dtype], *stats, sh)
+    _check(rc, "attn_decode_paged")
+    return out, (m_out if want_stats else None), (l_out if want_stats else None)
+
+
 def attn_fwd_raw(q_ptr, k_ptr, v_ptr, out_ptr, b, h, nq, nk, d, causal, scale, dtype,
                  stream_handle=0):
     """Direct C call with raw device pointers; returns the status code."""

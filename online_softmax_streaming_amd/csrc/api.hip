@@ -268,6 +268,96 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
   return ATTN_OK;
 }
 
+int attn_decode_paged(const void* Q, const void* K_cache, const void* V_cache,
+                      const int32_t* block_table, const int32_t* seq_lens, void* out, int64_t B,
+                      int64_t H, int64_t Hkv, int64_t Nq, int64_t D, int64_t num_pages,
+                      int64_t page_size, int64_t max_pages, int causal, int64_t window,
+                      float scale, int dtype, float* m_out, float* l_out, void* stream) {
+  g_last_error[0] = '\0';
+  if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_E_INVALID, "dtype %d is not ATTN_F32, ATTN_F16 or ATTN_BF16", dtype);
+  if (causal != 0 && causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1, got %d", causal);
+  if (B < 0 || H < 0 || Nq < 0)
+    return fail(ATTN_E_INVALID, "negative size (B=%lld H=%lld Nq=%lld)", (long long)B,
+                (long long)H, (long long)Nq);
+  if (H > 0 && (Hkv < 1 || Hkv > H || H % Hkv != 0))
+    return fail(ATTN_E_INVALID, "Hkv=%lld must divide H=%lld", (long long)Hkv, (long long)H);
+  if (D <= 0) return fail(ATTN_E_INVALID, "D must be positive, got %lld", (long long)D);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(ATTN_E_INVALID, "scale must be finite and > 0, got %g", (double)scale);
+  if (window < 0) return fail(ATTN_E_INVALID, "window must be >= 0, got %lld", (long long)window);
+  if (window > 0 && causal != 1)
+    return fail(ATTN_E_INVALID, "a sliding window needs causal = 1");
+  if (page_size < 1 || (page_size & (page_size - 1)) != 0 || page_size > (1 << 20))
+    return fail(ATTN_E_INVALID, "page_size must be a power of two in [1, 2^20], got %lld",
+                (long long)page_size);
+  if (num_pages < 1 || max_pages < 1 || num_pages > kI32Max || max_pages * page_size > kI32Max)
+    return fail(ATTN_E_INVALID, "need num_pages >= 1, max_pages >= 1, num_pages < 2^31 and "
+                                "max_pages * page_size < 2^31");
+  if (D != 16 && D != 32 && D != 64 && D != 128)
+    return fail(ATTN_E_UNSUPPORTED, "head size D=%lld not built (16, 32, 64, 128)", (long long)D);
+  if (B > kI32Max || H > kI32Max || Nq > kI32Max || B * H > kI32Max || B * H * Nq > kI32Max ||
+      B > kI32Max / max_pages)
+    return fail(ATTN_E_INVALID, "sizes exceed the 32-bit limits (B*H*Nq, B*max_pages < 2^31)");
+  if (B == 0 || H == 0 || Nq == 0) return ATTN_OK;
+
+  const int64_t elem = dtype == ATTN_F32 ? 4 : 2;
+  if (!Q || !K_cache || !V_cache || !block_table || !seq_lens || !out)
+    return fail(ATTN_E_INVALID, "Q, K_cache, V_cache, block_table, seq_lens and out must be non-NULL");
+  if (!aligned(Q, 16) || !aligned(K_cache, 16) || !aligned(V_cache, 16) || !aligned(out, 16))
+    return fail(ATTN_E_INVALID, "Q, K_cache, V_cache and out must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (m_out && !aligned(m_out, 4)) ||
+      (l_out && !aligned(l_out, 4)))
+    return fail(ATTN_E_INVALID, "block_table, seq_lens, m_out and l_out must be 4-byte aligned");
+  if (num_pages > INT64_MAX / Hkv / page_size / D / elem)
+    return fail(ATTN_E_INVALID, "cache size overflows 64 bits");
+  const int64_t qbytes = B * H * Nq * D * elem;
+  const int64_t cbytes = num_pages * Hkv * page_size * D * elem;
+  const int64_t sbytes = B * H * Nq * 4;
+  if (overlaps(out, qbytes, Q, qbytes) || overlaps(out, qbytes, K_cache, cbytes) ||
+      overlaps(out, qbytes, V_cache, cbytes) || overlaps(out, qbytes, block_table, B * max_pages * 4) ||
+      overlaps(out, qbytes, seq_lens, B * 4))
+    return fail(ATTN_E_INVALID, "out overlaps an input");
+  if (overlaps(m_out, sbytes, out, qbytes) || overlaps(l_out, sbytes, out, qbytes) ||
+      overlaps(m_out, sbytes, l_out, sbytes))
+    return fail(ATTN_E_INVALID, "m_out / l_out overlap out or each other");
+
+  attn::Problem p;
+  p.q = Q;
+  p.k = K_cache;
+  p.v = V_cache;
+  p.o = out;
+  p.m_out = m_out;
+  p.l_out = l_out;
+  p.B = B;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = max_pages * page_size;
+  p.D = D;
+  p.causal = causal != 0;
+  p.scale = scale;
+  p.dtype = static_cast<attn::DType>(dtype);
+  p.stream = static_cast<hipStream_t>(stream);
+  p.window = window;
+  p.table = block_table;
+  p.lens = seq_lens;
+  p.max_pages = max_pages;
+  p.page_size = page_size;
+  p.num_pages = num_pages;
+
+  const attn::DecodePlan plan = attn::plan_decode(p);
+  keep_pool_memory();
+  void* scratch = nullptr;
+  hipError_t e = hipMallocAsync(&scratch, plan.scratch_bytes, p.stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of decode scratch");
+  e = attn::launch_decode(p, plan, static_cast<float*>(scratch));
+  const hipError_t ef = hipFreeAsync(scratch, p.stream);
+  if (e != hipSuccess) return hip_fail(e, "paged decode kernel launch");
+  if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of decode scratch");
+  return ATTN_OK;
+}
+
 int online_merge(double m1, double l1, double m2, double l2, double* m, double* l) {
   g_last_error[0] = '\0';
   if (!m || !l) return fail(ATTN_E_INVALID, "online_merge: m and l must be non-NULL");

@@ -24,6 +24,12 @@ struct Problem {
   float scale;
   DType dtype;
   hipStream_t stream;
+  // Decode options: a sliding window (0 = none) and a paged K/V cache
+  // (table == nullptr: the contiguous layout above).
+  int64_t window = 0;
+  const int* table = nullptr;  // [B, max_pages] physical page of each logical page
+  const int* lens = nullptr;   // [B] keys per sequence
+  int64_t max_pages = 0, page_size = 0, num_pages = 0;
 };
 
 // Streaming prefill on bf16/f16 matrix cores (prefill_mfma.hip).

@@ -19,6 +19,16 @@
 // for one multiply-add), so it runs on the vector ALUs: lanes read 16-byte
 // chunks, D/VEC lanes cover one key row, and each loop step keeps U rows
 // per lane group in flight.
+//
+// Two key layouts share the kernels: contiguous [B, Hkv, Nk, D], and a paged
+// cache [num_pages, Hkv, page_size, D] where an int32 table maps page p of
+// sequence b to a physical page and an int32 length gives each sequence's
+// key count (a KV-cache slice; the pages plan one for a later week).  A
+// sliding window (causal only) keeps the `window` keys ending at the row's
+// diagonal; the splits cover only the visible key range of each row.  Table
+// entries outside [0, num_pages) are read as absent keys and lengths are
+// clamped to [0, max_pages * page_size]: table values are never used to
+// address memory outside the cache.
 
 #include "attn_device.h"
 #include "attn_kernels.h"
@@ -37,8 +47,16 @@ struct DecodeArgs {
   int H, Nq, Nk;
   int group;  // query heads per K/V head
   int S;
-  int kps;  // keys per split
-  float c;  // scale * log2(e)
+  int kps;     // keys per split
+  int window;  // 0: none; else the visible keys end at the diagonal, at most this many
+  float c;     // scale * log2(e)
+  // Paged layout (PAGED kernels only).
+  const int* table;   // [B, max_pages]
+  const int* lens;    // [B]
+  int Hkv;
+  int max_pages;
+  int page_shift;     // log2(page_size)
+  int64_t num_pages;
 };
 
 constexpr int kThreads = 256;
@@ -48,7 +66,7 @@ template <> struct Vec16<__bf16> { typedef bf16x8 type; static constexpr int n =
 template <> struct Vec16<_Float16> { typedef f16x8 type; static constexpr int n = 8; };
 template <> struct Vec16<float> { typedef f32x4 type; static constexpr int n = 4; };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) {
   typedef typename Vec16<T>::type vec;
   constexpr int VEC = Vec16<T>::n;
@@ -61,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
 
   const int row = blockIdx.x;  // (b*H + h)*Nq + i
   const int split = blockIdx.y;
-  const int Nq = a.Nq, Nk = a.Nk;
+  const int Nq = a.Nq;
   const int bh = row / Nq;
   const int i = row - bh * Nq;
   const int tid = threadIdx.x;
@@ -70,8 +88,31 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
   const float c = a.c;
 
   // Query head (b, h) reads K/V head (b, h / group): bh / group.
-  const T* __restrict__ Kh = static_cast<const T*>(a.k) + (int64_t)(bh / a.group) * Nk * D;
-  const T* __restrict__ Vh = static_cast<const T*>(a.v) + (int64_t)(bh / a.group) * Nk * D;
+  int Nk = a.Nk;
+  const T* __restrict__ Kh;
+  const T* __restrict__ Vh;
+  const int* trow = nullptr;
+  int hk = 0;
+  if (PAGED) {
+    const int b = bh / a.H;
+    hk = (bh - b * a.H) / a.group;
+    trow = a.table + (int64_t)b * a.max_pages;
+    Nk = min(max(a.lens[b], 0), a.max_pages << a.page_shift);
+    Kh = static_cast<const T*>(a.k);
+    Vh = static_cast<const T*>(a.v);
+  } else {
+    Kh = static_cast<const T*>(a.k) + (int64_t)(bh / a.group) * Nk * D;
+    Vh = static_cast<const T*>(a.v) + (int64_t)(bh / a.group) * Nk * D;
+  }
+  // Element offset of key row j (the row's head block), or -1 if its page
+  // is outside the cache.
+  auto key_offset = [&](int j) -> int64_t {
+    if (!PAGED) return (int64_t)j * D;
+    const int page = trow[j >> a.page_shift];
+    if (page < 0 || page >= a.num_pages) return -1;
+    const int r = j & ((1 << a.page_shift) - 1);
+    return ((((int64_t)page * a.Hkv + hk) << a.page_shift) + r) * D;
+  };
 
   float qv[VEC];
   {
@@ -82,7 +123,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
 
   int kend = Nk;
   if (CAUSAL) kend = min(Nk, i + (Nk - Nq) + 1);
-  const int kb = split * a.kps;
+  const int kbeg = a.window > 0 ? max(0, i + (Nk - Nq) - a.window + 1) : 0;
+  const int kb = kbeg + split * a.kps;
   const int ke = min(kend, kb + a.kps);
 
   float m_run = kNegInf, l_run = 0.f;
@@ -96,9 +138,10 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int jj = j + u * G;
-      in[u] = jj < ke;
-      kv[u] = in[u] ? *reinterpret_cast<const vec*>(Kh + (int64_t)jj * D + sub * VEC) : vec{};
-      vv[u] = in[u] ? *reinterpret_cast<const vec*>(Vh + (int64_t)jj * D + sub * VEC) : vec{};
+      const int64_t ko = jj < ke ? key_offset(jj) : -1;
+      in[u] = ko >= 0;
+      kv[u] = in[u] ? *reinterpret_cast<const vec*>(Kh + ko + sub * VEC) : vec{};
+      vv[u] = in[u] ? *reinterpret_cast<const vec*>(Vh + ko + sub * VEC) : vec{};
     }
     float s[U];
     float mx = kNegInf;
@@ -182,7 +225,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
   }
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool PAGED>
 hipError_t launch_typed(const Problem& p, const DecodePlan& plan, float* scratch) {
   DecodeArgs a;
   a.q = p.q;
@@ -198,9 +241,17 @@ hipError_t launch_typed(const Problem& p, const DecodePlan& plan, float* scratch
   a.Nk = (int)p.Nk;
   a.S = plan.splits;
   a.kps = plan.keys_per_split;
+  a.window = (int)p.window;
   a.c = p.scale * kLog2e;
+  a.table = p.table;
+  a.lens = p.lens;
+  a.Hkv = (int)p.Hkv;
+  a.max_pages = (int)p.max_pages;
+  a.page_shift = 0;
+  while ((int64_t(1) << a.page_shift) < p.page_size) ++a.page_shift;
+  a.num_pages = p.num_pages;
   const int64_t rows = p.B * p.H * p.Nq;
-  hipLaunchKernelGGL((decode_partial_kernel<T, D, CAUSAL>), dim3((unsigned)rows, plan.splits),
+  hipLaunchKernelGGL((decode_partial_kernel<T, D, CAUSAL, PAGED>), dim3((unsigned)rows, plan.splits),
                      dim3(kThreads), 0, p.stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -210,8 +261,11 @@ hipError_t launch_typed(const Problem& p, const DecodePlan& plan, float* scratch
 
 template <typename T, int D>
 hipError_t launch_d(const Problem& p, const DecodePlan& plan, float* scratch) {
-  return p.causal ? launch_typed<T, D, true>(p, plan, scratch)
-                  : launch_typed<T, D, false>(p, plan, scratch);
+  if (p.table)
+    return p.causal ? launch_typed<T, D, true, true>(p, plan, scratch)
+                    : launch_typed<T, D, false, true>(p, plan, scratch);
+  return p.causal ? launch_typed<T, D, true, false>(p, plan, scratch)
+                  : launch_typed<T, D, false, false>(p, plan, scratch);
 }
 
 template <typename T>
@@ -229,16 +283,19 @@ hipError_t launch_t(const Problem& p, const DecodePlan& plan, float* scratch) {
 
 DecodePlan plan_decode(const Problem& p) {
   // Aim for >= 4096 workgroups (16 per CU) so the HBM stream is deep enough,
-  // but give each split at least 256 keys so the merge stays cheap.
+  // but give each split at least 256 keys so the merge stays cheap.  The
+  // splits cover the longest visible key range a row can have.
   const int64_t rows = p.B * p.H * p.Nq;
+  int64_t range = p.table ? p.max_pages * p.page_size : p.Nk;
+  if (p.window > 0 && p.window < range) range = p.window;
   const int64_t want = (4096 + rows - 1) / rows;
-  int64_t kps = (p.Nk + want - 1) / want;
+  int64_t kps = (range + want - 1) / want;
   if (kps < 256) kps = 256;
-  int64_t splits = (p.Nk + kps - 1) / kps;
+  int64_t splits = (range + kps - 1) / kps;
   if (splits < 1) splits = 1;
   if (splits > 65535) {  // grid.y limit
     splits = 65535;
-    kps = (p.Nk + splits - 1) / splits;
+    kps = (range + splits - 1) / splits;
   }
   DecodePlan plan;
   plan.splits = (int)splits;

@@ -273,3 +273,49 @@ def test_attn_bwd_rejects_bad_arguments(attn, kw, code):
                                 dict(b=0, q=0, k=0, v=0, o=0, do=0, m=0, l=0, dq=0, dk=0, dv=0)])
 def test_attn_bwd_empty_is_a_noop(attn, kw):
     assert _bwd(attn, **kw) == 0
+
+
+def _paged(attn, **kw):
+    from online_softmax_streaming_amd import _lib
+    g = 1 << 24
+    a = dict(q=1 * g, kc=2 * g, vc=4 * g, table=6 * g, lens=7 * g, out=8 * g, b=2, h=4, hkv=2,
+             nq=1, d=64, num_pages=16, page_size=16, max_pages=8, causal=1, window=0,
+             scale=0.125, dtype=2, m=None, l=None)
+    a.update(kw)
+    return _lib.lib().attn_decode_paged(a["q"], a["kc"], a["vc"], a["table"], a["lens"], a["out"],
+                                        a["b"], a["h"], a["hkv"], a["nq"], a["d"],
+                                        a["num_pages"], a["page_size"], a["max_pages"],
+                                        a["causal"], a["window"], a["scale"], a["dtype"],
+                                        a["m"], a["l"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), 1),
+    (dict(causal=2), 1),
+    (dict(hkv=3), 1),
+    (dict(d=48), 2),
+    (dict(scale=-1.0), 1),
+    (dict(window=-1), 1),
+    (dict(window=4, causal=0), 1),          # a window needs causal attention
+    (dict(page_size=12), 1),                # not a power of two
+    (dict(page_size=0), 1),
+    (dict(num_pages=0), 1),
+    (dict(max_pages=0), 1),
+    (dict(max_pages=1 << 27, page_size=16), 1),  # max_pages * page_size reaches 2^31
+    (dict(q=0), 1),
+    (dict(table=0), 1),
+    (dict(lens=0), 1),
+    (dict(kc=2 * (1 << 24) + 8), 1),        # misaligned cache
+    (dict(table=6 * (1 << 24) + 2), 1),     # misaligned table
+    (dict(out=2 * (1 << 24)), 1),           # out overlaps K_cache
+    (dict(out=6 * (1 << 24)), 1),           # out overlaps the table
+])
+def test_attn_decode_paged_rejects_bad_arguments(attn, kw, code):
+    from online_softmax_streaming_amd import _lib
+    assert _paged(attn, **kw) == code, _lib.lib().attn_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(b=0), dict(h=0), dict(nq=0),
+                                dict(b=0, q=0, kc=0, vc=0, table=0, lens=0, out=0)])
+def test_attn_decode_paged_empty_is_a_noop(attn, kw):
+    assert _paged(attn, **kw) == 0

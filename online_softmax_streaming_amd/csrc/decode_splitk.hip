@@ -104,16 +104,6 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
     Kh = static_cast<const T*>(a.k) + (int64_t)(bh / a.group) * Nk * D;
     Vh = static_cast<const T*>(a.v) + (int64_t)(bh / a.group) * Nk * D;
   }
-  // Element offset of key row j (the row's head block), or -1 if its page
-  // is outside the cache.
-  auto key_offset = [&](int j) -> int64_t {
-    if (!PAGED) return (int64_t)j * D;
-    const int page = trow[j >> a.page_shift];
-    if (page < 0 || page >= a.num_pages) return -1;
-    const int r = j & ((1 << a.page_shift) - 1);
-    return ((((int64_t)page * a.Hkv + hk) << a.page_shift) + r) * D;
-  };
-
   float qv[VEC];
   {
     const vec q = *reinterpret_cast<const vec*>(static_cast<const T*>(a.q) + (int64_t)row * D + sub * VEC);
@@ -132,13 +122,36 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
 
-  for (int j = kb + g; j < ke; j += G * U) {
-    vec kv[U], vv[U];
-    bool in[U];
+  // Paged: the page indices of a step are fetched one step ahead, so the
+  // table read is not in series with the key reads it addresses.
+  int pg[U];
+  auto fetch_pages = [&](int j) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int jj = j + u * G;
-      const int64_t ko = jj < ke ? key_offset(jj) : -1;
+      pg[u] = PAGED && jj < ke ? trow[jj >> a.page_shift] : 0;
+    }
+  };
+  if (PAGED) fetch_pages(kb + g);
+  for (int j = kb + g; j < ke; j += G * U) {
+    vec kv[U], vv[U];
+    bool in[U];
+    int cur[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = pg[u];
+    if (PAGED) fetch_pages(j + G * U);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jj = j + u * G;
+      int64_t ko = -1;
+      if (jj < ke) {
+        if (!PAGED) {
+          ko = (int64_t)jj * D;
+        } else if (cur[u] >= 0 && cur[u] < a.num_pages) {
+          const int r = jj & ((1 << a.page_shift) - 1);
+          ko = ((((int64_t)cur[u] * a.Hkv + hk) << a.page_shift) + r) * D;
+        }
+      }
       in[u] = ko >= 0;
       kv[u] = in[u] ? *reinterpret_cast<const vec*>(Kh + ko + sub * VEC) : vec{};
       vv[u] = in[u] ? *reinterpret_cast<const vec*>(Vh + ko + sub * VEC) : vec{};

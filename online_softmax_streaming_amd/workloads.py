@@ -117,35 +117,37 @@ def make_paged(B, H, Hkv, Nq, D, page_size, seq_lens, dtype, seed=0, device="cpu
     """Inputs of a paged-cache decode: (q, k_cache, v_cache, block_table, seq_lens).
 
     q [B, H, Nq, D] and the caches [num_pages, Hkv, page_size, D] are
-    N(0, 1) FP32 from one generator seeded with ``seed`` (drawn in the order
-    q, K cache, V cache), rounded to ``dtype``.  Each sequence gets
+    N(0, 1) FP32 from one generator seeded with ``seed`` on ``device``
+    (drawn in the order q, K cache, V cache), rounded to ``dtype``.  Each sequence gets
     ceil(len / page_size) pages from a seeded permutation of all pages (plus
     ``spare_pages`` unused ones), so logical order and physical order
     differ; table entries past a sequence's pages are -1 (never read).
     ``share_first_page`` makes sequence 1 reuse sequence 0's first page
     (a shared prefix).
     """
-    g = torch.Generator(device="cpu")
+    gen_device = "cpu" if str(device) == "cpu" else device
+    g = torch.Generator(device=gen_device)
     g.manual_seed(seed)
     npp = [(int(n) + page_size - 1) // page_size for n in seq_lens]
     max_pages = max(1, max(npp) if npp else 1)
     total = sum(npp) + spare_pages
-    q = torch.randn((B, H, Nq, D), generator=g, dtype=torch.float32)
-    kc = torch.randn((total, Hkv, page_size, D), generator=g, dtype=torch.float32)
-    vc = torch.randn((total, Hkv, page_size, D), generator=g, dtype=torch.float32)
-    perm = torch.randperm(total, generator=g)
+    dt = DTYPES[dtype]
+    q = torch.randn((B, H, Nq, D), generator=g, dtype=torch.float32, device=gen_device).to(dt)
+    kc = torch.randn((total, Hkv, page_size, D), generator=g, dtype=torch.float32,
+                     device=gen_device).to(dt)
+    vc = torch.randn((total, Hkv, page_size, D), generator=g, dtype=torch.float32,
+                     device=gen_device).to(dt)
+    perm = torch.randperm(total, generator=g, device=gen_device).to("cpu")
     table = torch.full((B, max_pages), -1, dtype=torch.int32)
-    nxt = 0
+    offs = [0]
+    for n in npp:
+        offs.append(offs[-1] + n)
     for b in range(B):
-        for p in range(npp[b]):
-            table[b, p] = int(perm[nxt])
-            nxt += 1
+        table[b, :npp[b]] = perm[offs[b]:offs[b + 1]].to(torch.int32)
     if share_first_page and B > 1 and npp[0] > 0 and npp[1] > 0:
         table[1, 0] = table[0, 0]
     lens = torch.tensor([int(n) for n in seq_lens], dtype=torch.int32)
-    dt = DTYPES[dtype]
-    return (q.to(device=device, dtype=dt), kc.to(device=device, dtype=dt),
-            vc.to(device=device, dtype=dt), table.to(device), lens.to(device))
+    return (q.to(device), kc.to(device), vc.to(device), table.to(device), lens.to(device))
 
 
 @dataclasses.dataclass(frozen=True)

@@ -40,6 +40,7 @@ from .softmax import (  # noqa: F401
     split_softmax_model,
 )
 from .paged import attention_paged, gather_pages  # noqa: F401
+from .varlen import attention_varlen  # noqa: F401
 from .attention_backward import (  # noqa: F401
     attention_backward,
     attention_backward_head,

@@ -175,6 +175,47 @@ ATTN_API int attn_bwd(const void* Q, const void* K, const void* V, const void* O
                       int64_t D, int causal, float scale, int dtype, void* stream);
 
 /*
+ * attn_fwd_varlen -- attention over a batch of packed sequences of
+ * different lengths (the padding lengths that [W] "Scope and contracts"
+ * lists as an extension opportunity, in packed form; per sequence the
+ * computation is attn_fwd_gqa's, [AK] row A3).
+ *
+ * B sequences are concatenated along the token axis.  Sequence b owns query
+ * rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] ..
+ * cu_seqlens_k[b+1]-1, and attends only to its own keys; query head h reads
+ * K/V head h / (H / Hkv); causal keys are aligned to the end of the
+ * sequence's own query block (j <= i + Nk_b - Nq_b).  Empty sequences and
+ * sequences with no keys are allowed (rows without a visible key get 0).
+ *
+ * Layout (token-major, D fastest): Q and out contiguous [total_q, H, D]; K
+ * and V contiguous [total_k, Hkv, D]; cu_seqlens_q/k int32 [B + 1]
+ * (non-decreasing, first 0, last total_q / total_k); m_out, l_out optional
+ * FP32 [H, total_q] (head-major) with attn_fwd_stats' meaning.  dtype and
+ * arithmetic as attn_fwd.
+ *
+ * Arguments:
+ *   max_seqlen_q  the longest query sequence (sizes the grid; 0 <= it <=
+ *                 total_q).  Rows of a longer sequence are not written.
+ *   cu_seqlens_*  device arrays, 4-byte aligned.  Values are not scanned:
+ *                 each bound is clamped into [0, total] and made
+ *                 non-decreasing, so no value addresses memory outside the
+ *                 tensors.
+ *   Q, K, V, out  16-byte aligned device pointers (K, V may be NULL if
+ *                 total_k == 0); out must not overlap an input.
+ *   Limits: total_q, total_k, B*H*max_seqlen_q < 2^31; packed K (and V)
+ *   at most 4 GiB (else ATTN_E_UNSUPPORTED).  B, H or total_q == 0 is a
+ *   no-op.  D, causal, scale, dtype, stream as attn_fwd.
+ * Memory: allocates nothing.  Returns ATTN_OK once queued, else the status
+ * codes of attn_fwd.
+ */
+ATTN_API int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* out,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             int64_t B, int64_t H, int64_t Hkv, int64_t total_q,
+                             int64_t total_k, int64_t max_seqlen_q, int64_t D, int causal,
+                             float scale, int dtype, float* m_out, float* l_out,
+                             void* stream);
+
+/*
  * attn_decode_paged -- attention of a few query rows per head over a paged
  * key/value cache, with an optional sliding window (a KV-cache slice and a
  * sliding window: the decode variants the workshops page plans for a later

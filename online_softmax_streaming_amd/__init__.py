@@ -21,6 +21,7 @@ from .attn import (  # noqa: F401
     attn_fwd_gqa,
     attn_fwd_raw,
     attn_fwd_stats,
+    attn_fwd_varlen,
     attn_strerror,
     default_scale,
     online_merge,

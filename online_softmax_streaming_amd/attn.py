@@ -181,6 +181,58 @@ def attn_bwd(q, k, v, out, dout, m, l, causal=False, scale=None, dq=None, dk=Non
     return dq, dk, dv
 
 
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, causal=False,
+                    scale=None, out=None, want_stats=False, stream=None):
+    """Attention over packed sequences of different lengths; returns
+    (out, m, l) (m, l None unless ``want_stats``; head-major [H, total_q]).
+
+    q: [total_q, H, D]; k, v: [total_k, Hkv, D] (Hkv dividing H); one
+    dtype, contiguous, on one GPU.  cu_seqlens_q / cu_seqlens_k: int32
+    [B + 1] offsets of each sequence's first row.  ``max_seqlen_q``: the
+    longest query sequence; when None it is read from cu_seqlens_q, which
+    synchronises the host with the device.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dim() != 3:
+            raise ValueError(f"{name} must be a 3-D GPU tensor [total, heads, D]")
+        if not t.is_contiguous() or t.dtype not in _DTYPES or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be contiguous and share q's dtype")
+    if k.shape != v.shape or k.shape[2] != q.shape[2]:
+        raise ValueError("k and v must match and share q's D")
+    total_q, h, d = q.shape
+    total_k, hkv, _ = k.shape
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.device != q.device
+                or t.dim() != 1 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 1-D GPU tensor")
+    if cu_seqlens_q.shape != cu_seqlens_k.shape or cu_seqlens_q.shape[0] < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B + 1]")
+    b = cu_seqlens_q.shape[0] - 1
+    if max_seqlen_q is None:
+        max_seqlen_q = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if b else 0
+    if scale is None:
+        scale = default_scale(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor like q")
+    m = l = None
+    if want_stats:
+        m = torch.empty((h, total_q), dtype=torch.float32, device=q.device)
+        l = torch.empty((h, total_q), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        sh = _stream_handle(stream, q.device)
+        stats = ((ctypes.c_void_p(m.data_ptr()), ctypes.c_void_p(l.data_ptr()))
+                 if want_stats else (None, None))
+        rc = lib().attn_fwd_varlen(
+            *(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out, cu_seqlens_q, cu_seqlens_k)),
+            b, h, hkv, total_q, total_k, int(max_seqlen_q), d, int(bool(causal)), float(scale),
+            _DTYPES[q.dtype], *stats, sh)
+    _check(rc, "attn_fwd_varlen")
+    return out, m, l
+
+
 def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, causal=True, window=0,
                       scale=None, out=None, m_out=None, l_out=None, want_stats=False,
                       stream=None):

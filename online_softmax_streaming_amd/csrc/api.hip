@@ -358,6 +358,85 @@ int attn_decode_paged(const void* Q, const void* K_cache, const void* V_cache,
   return ATTN_OK;
 }
 
+int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* out,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t B,
+                    int64_t H, int64_t Hkv, int64_t total_q, int64_t total_k,
+                    int64_t max_seqlen_q, int64_t D, int causal, float scale, int dtype,
+                    float* m_out, float* l_out, void* stream) {
+  g_last_error[0] = '\0';
+  if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_E_INVALID, "dtype %d is not ATTN_F32, ATTN_F16 or ATTN_BF16", dtype);
+  if (causal != 0 && causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1, got %d", causal);
+  if (B < 0 || H < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0)
+    return fail(ATTN_E_INVALID, "negative size (B=%lld H=%lld total_q=%lld total_k=%lld "
+                "max_seqlen_q=%lld)", (long long)B, (long long)H, (long long)total_q,
+                (long long)total_k, (long long)max_seqlen_q);
+  if (H > 0 && (Hkv < 1 || Hkv > H || H % Hkv != 0))
+    return fail(ATTN_E_INVALID, "Hkv=%lld must divide H=%lld", (long long)Hkv, (long long)H);
+  if (D <= 0) return fail(ATTN_E_INVALID, "D must be positive, got %lld", (long long)D);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(ATTN_E_INVALID, "scale must be finite and > 0, got %g", (double)scale);
+  if (max_seqlen_q > total_q)
+    return fail(ATTN_E_INVALID, "max_seqlen_q=%lld exceeds total_q=%lld", (long long)max_seqlen_q,
+                (long long)total_q);
+  if (D != 16 && D != 32 && D != 64 && D != 128)
+    return fail(ATTN_E_UNSUPPORTED, "head size D=%lld not built (16, 32, 64, 128)", (long long)D);
+  if (B > kI32Max - 1 || H > kI32Max || total_q > kI32Max || total_k > kI32Max ||
+      B * H > kI32Max || B * H * max_seqlen_q > kI32Max)
+    return fail(ATTN_E_INVALID, "sizes exceed the 32-bit limits (B*H*max_seqlen_q, total_q, "
+                                "total_k < 2^31)");
+  const int64_t elem = dtype == ATTN_F32 ? 4 : 2;
+  if (total_k * Hkv * D * elem > 4294967295LL)
+    return fail(ATTN_E_UNSUPPORTED, "packed K and V above 4 GiB each are not supported");
+  if (B == 0 || H == 0 || total_q == 0) return ATTN_OK;
+
+  if (!Q || !out || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(ATTN_E_INVALID, "Q, out, cu_seqlens_q and cu_seqlens_k must be non-NULL");
+  if (total_k > 0 && (!K || !V))
+    return fail(ATTN_E_INVALID, "K and V must be non-NULL when total_k > 0");
+  if (!aligned(Q, 16) || !aligned(out, 16) || (total_k > 0 && (!aligned(K, 16) || !aligned(V, 16))))
+    return fail(ATTN_E_INVALID, "Q, K, V and out must be 16-byte aligned");
+  if (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || (m_out && !aligned(m_out, 4)) ||
+      (l_out && !aligned(l_out, 4)))
+    return fail(ATTN_E_INVALID, "cu_seqlens_q/k, m_out and l_out must be 4-byte aligned");
+  const int64_t qbytes = total_q * H * D * elem;
+  const int64_t kbytes = total_k * Hkv * D * elem;
+  const int64_t sbytes = total_q * H * 4;
+  if (overlaps(out, qbytes, Q, qbytes) || overlaps(out, qbytes, K, kbytes) ||
+      overlaps(out, qbytes, V, kbytes) || overlaps(out, qbytes, cu_seqlens_q, (B + 1) * 4) ||
+      overlaps(out, qbytes, cu_seqlens_k, (B + 1) * 4))
+    return fail(ATTN_E_INVALID, "out overlaps an input");
+  if (overlaps(m_out, sbytes, out, qbytes) || overlaps(l_out, sbytes, out, qbytes) ||
+      overlaps(m_out, sbytes, l_out, sbytes))
+    return fail(ATTN_E_INVALID, "m_out / l_out overlap out or each other");
+  if (max_seqlen_q == 0) return ATTN_OK;  // every sequence is empty
+
+  attn::Problem p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = out;
+  p.m_out = m_out;
+  p.l_out = l_out;
+  p.B = B;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.Nq = max_seqlen_q;
+  p.Nk = 0;
+  p.D = D;
+  p.causal = causal != 0;
+  p.scale = scale;
+  p.dtype = static_cast<attn::DType>(dtype);
+  p.stream = static_cast<hipStream_t>(stream);
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  const hipError_t e =
+      dtype == ATTN_F32 ? attn::launch_prefill_f32(p) : attn::launch_prefill_mfma(p);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "varlen prefill kernel launch");
+}
+
 int online_merge(double m1, double l1, double m2, double l2, double* m, double* l) {
   g_last_error[0] = '\0';
   if (!m || !l) return fail(ATTN_E_INVALID, "online_merge: m and l must be non-NULL");

@@ -30,6 +30,12 @@ struct Problem {
   const int* table = nullptr;  // [B, max_pages] physical page of each logical page
   const int* lens = nullptr;   // [B] keys per sequence
   int64_t max_pages = 0, page_size = 0, num_pages = 0;
+  // Packed variable-length sequences (prefill kernels; cu_q == nullptr: the
+  // batched layout).  Q/out [total_q, H, D], K/V [total_k, Hkv, D]; Nq is
+  // the longest query sequence; row states [H, total_q].
+  const int* cu_q = nullptr;  // [B + 1]
+  const int* cu_k = nullptr;  // [B + 1]
+  int64_t total_q = 0, total_k = 0;
 };
 
 // Streaming prefill on bf16/f16 matrix cores (prefill_mfma.hip).

@@ -29,12 +29,18 @@ struct F32Args {
   int nqt;
   int group;  // query heads per K/V head
   float c;  // scale * log2(e)
+  // Packed variable-length sequences (VARLEN only), as in the matrix-core
+  // kernel: Q/out [total_q, H, D], K/V [total_k, Hkv, D], states [H, total_q].
+  const int* cu_q;
+  const int* cu_k;
+  int H, Hkv;
+  int total_q, total_k;
 };
 
 constexpr int kThreads = 128;
 constexpr int kBNF = 32;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
   constexpr int TPQ = D > 64 ? 2 : 1;
   constexpr int DT = D / TPQ;
@@ -46,11 +52,33 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
 
   const int bh = blockIdx.x / a.nqt;
   const int qt = blockIdx.x - bh * a.nqt;
-  const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
-  const float* __restrict__ Qh = a.q + (int64_t)bh * Nq * D;
-  const float* __restrict__ Kh = a.k + (int64_t)(bh / a.group) * Nk * D;  // K/V head bh / group
-  const float* __restrict__ Vh = a.v + (int64_t)(bh / a.group) * Nk * D;
-  float* __restrict__ Oh = a.o + (int64_t)bh * Nq * D;
+  int Nq = a.Nq, Nk = a.Nk;
+  int64_t qbase, kbase, stat0, sq = D, sk = D;
+  if (VARLEN) {
+    // Sequence bounds clamped into the packed tensors (see prefill_mfma).
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int q0 = min(max(a.cu_q[b], 0), a.total_q);
+    const int q1 = min(max(a.cu_q[b + 1], q0), a.total_q);
+    const int k0 = min(max(a.cu_k[b], 0), a.total_k);
+    const int k1 = min(max(a.cu_k[b + 1], k0), a.total_k);
+    Nq = q1 - q0;
+    Nk = k1 - k0;
+    if (qt * QPB >= Nq) return;
+    sq = (int64_t)a.H * D;
+    sk = (int64_t)a.Hkv * D;
+    qbase = (int64_t)q0 * sq + (int64_t)h * D;
+    kbase = (int64_t)k0 * sk + (int64_t)(h / a.group) * D;
+    stat0 = (int64_t)h * a.total_q + q0;
+  } else {
+    qbase = (int64_t)bh * Nq * D;
+    kbase = (int64_t)(bh / a.group) * Nk * D;  // K/V head bh / group
+    stat0 = (int64_t)bh * Nq;
+  }
+  const int off = Nk - Nq;
+  const float* __restrict__ Qh = a.q + qbase;
+  const float* __restrict__ Kh = a.k + kbase;
+  const float* __restrict__ Vh = a.v + kbase;
+  float* __restrict__ Oh = a.o + qbase;
 
   const int tid = threadIdx.x;
   const int part = tid % TPQ;
@@ -61,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
   float q[DT], acc[DT];
 #pragma unroll
   for (int d = 0; d < DT; ++d) {
-    q[d] = qrow < Nq ? Qh[(int64_t)qrow * D + part * DT + d] : 0.f;
+    q[d] = qrow < Nq ? Qh[(int64_t)qrow * sq + part * DT + d] : 0.f;
     acc[d] = 0.f;
   }
   float m_run = kNegInf, l_run = 0.f;
@@ -78,8 +106,8 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
       const int j = j0 + row;
       f32x4 kv = f32x4{}, vv = f32x4{};
       if (j < Nk) {
-        kv = *reinterpret_cast<const f32x4*>(Kh + (int64_t)j * D + col * 4);
-        vv = *reinterpret_cast<const f32x4*>(Vh + (int64_t)j * D + col * 4);
+        kv = *reinterpret_cast<const f32x4*>(Kh + (int64_t)j * sk + col * 4);
+        vv = *reinterpret_cast<const f32x4*>(Vh + (int64_t)j * sk + col * 4);
       }
       *reinterpret_cast<f32x4*>(&Ks[row * D + col * 4]) = kv;
       *reinterpret_cast<f32x4*>(&Vs[row * D + col * 4]) = vv;
@@ -125,16 +153,16 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
   if (qrow < Nq) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
-    for (int d = 0; d < DT; ++d) Oh[(int64_t)qrow * D + part * DT + d] = acc[d] * inv;
+    for (int d = 0; d < DT; ++d) Oh[(int64_t)qrow * sq + part * DT + d] = acc[d] * inv;
     if (part == 0) {
-      const int64_t row = (int64_t)bh * Nq + qrow;
+      const int64_t row = stat0 + qrow;
       if (a.m_out) a.m_out[row] = m_run * kLn2;
       if (a.l_out) a.l_out[row] = l_run;
     }
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_typed(const Problem& p) {
   constexpr int TPQ = D > 64 ? 2 : 1;
   constexpr int QPB = kThreads / TPQ;
@@ -150,15 +178,22 @@ hipError_t launch_typed(const Problem& p) {
   a.nqt = (int)((p.Nq + QPB - 1) / QPB);
   a.group = (int)(p.H / p.Hkv);
   a.c = p.scale * kLog2e;
+  a.cu_q = p.cu_q;
+  a.cu_k = p.cu_k;
+  a.H = (int)p.H;
+  a.Hkv = (int)p.Hkv;
+  a.total_q = (int)p.total_q;
+  a.total_k = (int)p.total_k;
   const int64_t grid = p.B * p.H * a.nqt;
-  hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(kThreads), 0,
                      p.stream, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const Problem& p) {
-  return p.causal ? launch_typed<D, true>(p) : launch_typed<D, false>(p);
+  if (p.cu_q) return p.causal ? launch_typed<D, true, true>(p) : launch_typed<D, false, true>(p);
+  return p.causal ? launch_typed<D, true, false>(p) : launch_typed<D, false, false>(p);
 }
 
 }  // namespace

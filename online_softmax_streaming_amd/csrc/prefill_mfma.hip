@@ -67,6 +67,14 @@ struct PrefillArgs {
   int total;    // (B*H) * nwork real workgroups
   int per_xcd;  // gridDim.x / 8
   float c;      // scale * log2(e)
+  // Packed variable-length sequences (VARLEN kernels only): Q/out are
+  // [total_q, H, D], K/V [total_k, Hkv, D], sequence b owns rows
+  // cu_q[b] .. cu_q[b+1]-1 and keys cu_k[b] .. cu_k[b+1]-1; row states are
+  // [H, total_q].  nqt is then the tile count of the longest sequence.
+  const int* cu_q;
+  const int* cu_k;
+  int H, Hkv;
+  int total_q, total_k;
 };
 
 constexpr int kBN = 64;              // keys per tile
@@ -81,7 +89,7 @@ constexpr int kKPF = ATTN_KPF;
 constexpr int kVPF = ATTN_VPF;
 constexpr float kRefreshGap = 8.0f;  // base-2 units; see the file comment
 
-template <typename T, int D, int NW, bool CAUSAL>
+template <typename T, int D, int NW, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_mfma_kernel(PrefillArgs a) {
   typedef typename Mfma<T>::vec8 vec8;
@@ -117,16 +125,44 @@ void prefill_mfma_kernel(PrefillArgs a) {
   if (logical >= a.total) return;
   const int bh = logical / a.nwork;
   const int rr = logical - bh * a.nwork;
-  const int npass = CAUSAL && a.nqt - 1 - rr != rr ? 2 : 1;
-  for (int pass = 0; pass < npass; ++pass) {
-    const int qt = CAUSAL ? (pass == 0 ? a.nqt - 1 - rr : rr) : rr;
 
-    const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
-    const T* __restrict__ Qh = static_cast<const T*>(a.q) + (int64_t)bh * Nq * D;
+  // This head's rows: element offsets of Q/out and K/V row 0, row strides,
+  // and the row-state index of query row 0 (stride 1).
+  int Nq = a.Nq, Nk = a.Nk, nqt = a.nqt;
+  int64_t qbase, kbase, stat0;
+  int64_t sq = D, sk = D;
+  if (VARLEN) {
+    // Sequence bounds are clamped into the packed tensors, so no value of
+    // cu_q / cu_k can address memory outside them.
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int q0 = min(max(a.cu_q[b], 0), a.total_q);
+    const int q1 = min(max(a.cu_q[b + 1], q0), a.total_q);
+    const int k0 = min(max(a.cu_k[b], 0), a.total_k);
+    const int k1 = min(max(a.cu_k[b + 1], k0), a.total_k);
+    Nq = q1 - q0;
+    Nk = k1 - k0;
+    nqt = (Nq + BM - 1) / BM;
+    if (rr >= (CAUSAL ? (nqt + 1) / 2 : nqt)) return;  // shorter than the longest sequence
+    sq = (int64_t)a.H * D;
+    sk = (int64_t)a.Hkv * D;
+    qbase = (int64_t)q0 * sq + (int64_t)h * D;
+    kbase = (int64_t)k0 * sk + (int64_t)(h / a.group) * D;
+    stat0 = (int64_t)h * a.total_q + q0;
+  } else {
+    qbase = (int64_t)bh * Nq * D;
     // Query head (b, h) reads K/V head (b, h / group): bh / group.
-    const T* Kh = static_cast<const T*>(a.k) + (int64_t)(bh / a.group) * Nk * D;
-    const T* Vh = static_cast<const T*>(a.v) + (int64_t)(bh / a.group) * Nk * D;
-    T* __restrict__ Oh = static_cast<T*>(a.o) + (int64_t)bh * Nq * D;
+    kbase = (int64_t)(bh / a.group) * Nk * D;
+    stat0 = (int64_t)bh * Nq;
+  }
+  const int npass = CAUSAL && nqt - 1 - rr != rr ? 2 : 1;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int qt = CAUSAL ? (pass == 0 ? nqt - 1 - rr : rr) : rr;
+
+    const int off = Nk - Nq;
+    const T* __restrict__ Qh = static_cast<const T*>(a.q) + qbase;
+    const T* Kh = static_cast<const T*>(a.k) + kbase;
+    const T* Vh = static_cast<const T*>(a.v) + kbase;
+    T* __restrict__ Oh = static_cast<T*>(a.o) + qbase;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -144,7 +180,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
   #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       qf[kc] = qrow < Nq
-                   ? *reinterpret_cast<const vec8*>(Qh + (int64_t)qrow * D + kc * 16 + h32 * 8)
+                   ? *reinterpret_cast<const vec8*>(Qh + (int64_t)qrow * sq + kc * 16 + h32 * 8)
                    : vec8{};
     }
 
@@ -154,8 +190,12 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
 
     // Buffer resources over this head's K and V: offsets at or past Nk rows
-    // are out of range and read as zero.
-    const uint32_t kv_bytes = (uint32_t)Nk * (uint32_t)(2 * D);
+    // are out of range and read as zero (rows are 2*sk bytes apart; the
+    // range ends at the last byte of row Nk-1).
+    const uint32_t kpitch = (uint32_t)(2 * sk);
+    const uint32_t kv_bytes =
+        VARLEN ? (Nk > 0 ? (uint32_t)(Nk - 1) * kpitch + (uint32_t)(2 * D) : 0u)
+               : (uint32_t)Nk * (uint32_t)(2 * D);
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(Kh), 0, (int)kv_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
@@ -212,7 +252,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
           const int row = sl / G::CPR;
           const int chunk = (sl % G::CPR) ^ G::swz(row);
           const int j = min(j0 + row, Nk);  // rows past Nk: out of range, read as 0
-          const uint32_t vo = (uint32_t)j * (uint32_t)(2 * D) + (uint32_t)(chunk << 4);
+          const uint32_t vo = (uint32_t)j * kpitch + (uint32_t)(chunk << 4);
           __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, LDS_PTR(void, tile_ptr(buf, 0) + sl0 * 16),
                                                    16, (int)vo, 0, 0, 0);
           __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, LDS_PTR(void, tile_ptr(buf, 1) + sl0 * 16),
@@ -354,7 +394,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const float l_tot = half_sum(l_run);
     if (qrow < Nq) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      T* orow = Oh + (int64_t)qrow * D;
+      T* orow = Oh + (int64_t)qrow * sq;
   #pragma unroll
       for (int n = 0; n < NB; ++n) {
   #pragma unroll
@@ -370,7 +410,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
       }
       if (h32 == 0) {
         // Row state relative to the exact max: sum exp = l * e^m.
-        const int64_t row = (int64_t)bh * Nq + qrow;
+        const int64_t row = stat0 + qrow;
         const float to_true = m_true == kNegInf ? 0.f : exp2_hw(m_run - m_true);
         if (a.m_out) a.m_out[row] = m_true * kLn2;
         if (a.l_out) a.l_out[row] = l_tot * to_true;
@@ -379,7 +419,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
   }  // pass
 }
 
-template <typename T, int D, int NW, bool CAUSAL>
+template <typename T, int D, int NW, bool CAUSAL, bool VARLEN>
 hipError_t launch_typed(const Problem& p) {
   constexpr int BM = 32 * NW;
   PrefillArgs a;
@@ -392,14 +432,20 @@ hipError_t launch_typed(const Problem& p) {
   a.Nq = (int)p.Nq;
   a.Nk = (int)p.Nk;
   a.group = (int)(p.H / p.Hkv);
-  a.nqt = (int)((p.Nq + BM - 1) / BM);
+  a.nqt = (int)((p.Nq + BM - 1) / BM);  // varlen: p.Nq is the longest sequence
+  a.cu_q = p.cu_q;
+  a.cu_k = p.cu_k;
+  a.H = (int)p.H;
+  a.Hkv = (int)p.Hkv;
+  a.total_q = (int)p.total_q;
+  a.total_k = (int)p.total_k;
   a.nwork = CAUSAL ? (a.nqt + 1) / 2 : a.nqt;
   const int64_t total = p.B * p.H * a.nwork;
   a.total = (int)total;
   const int64_t grid = (total + 7) / 8 * 8;
   a.per_xcd = (int)(grid / 8);
   a.c = p.scale * kLog2e;
-  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, NW, CAUSAL>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, NW, CAUSAL, VARLEN>), dim3((unsigned)grid),
                      dim3(NW * 64), 0, p.stream, a);
   return hipGetLastError();
 }
@@ -412,7 +458,11 @@ constexpr int kWaves = ATTN_PREFILL_WAVES;
 
 template <typename T, int D>
 hipError_t launch_d(const Problem& p) {
-  return p.causal ? launch_typed<T, D, kWaves, true>(p) : launch_typed<T, D, kWaves, false>(p);
+  if (p.cu_q)
+    return p.causal ? launch_typed<T, D, kWaves, true, true>(p)
+                    : launch_typed<T, D, kWaves, false, true>(p);
+  return p.causal ? launch_typed<T, D, kWaves, true, false>(p)
+                  : launch_typed<T, D, kWaves, false, false>(p);
 }
 
 template <typename T>

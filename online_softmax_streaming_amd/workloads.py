@@ -9,6 +9,7 @@ rising key offset pushes the running max up tile after tile).
 """
 
 import dataclasses
+import itertools
 
 import torch
 
@@ -148,6 +149,23 @@ def make_paged(B, H, Hkv, Nq, D, page_size, seq_lens, dtype, seed=0, device="cpu
         table[1, 0] = table[0, 0]
     lens = torch.tensor([int(n) for n in seq_lens], dtype=torch.int32)
     return (q.to(device), kc.to(device), vc.to(device), table.to(device), lens.to(device))
+
+
+def make_varlen(lens_q, lens_k, H, Hkv, D, dtype, seed=0, device="cpu"):
+    """Packed variable-length inputs: (q [total_q, H, D], k, v [total_k, Hkv, D],
+    cu_q, cu_k int32 [B + 1]); N(0, 1) FP32 from one generator seeded with
+    ``seed`` on ``device``, drawn in the order q, k, v, rounded to ``dtype``."""
+    gen_device = "cpu" if str(device) == "cpu" else device
+    g = torch.Generator(device=gen_device)
+    g.manual_seed(seed)
+    tq, tk = int(sum(lens_q)), int(sum(lens_k))
+    dt = DTYPES[dtype]
+    q = torch.randn((tq, H, D), generator=g, dtype=torch.float32, device=gen_device).to(dt)
+    k = torch.randn((tk, Hkv, D), generator=g, dtype=torch.float32, device=gen_device).to(dt)
+    v = torch.randn((tk, Hkv, D), generator=g, dtype=torch.float32, device=gen_device).to(dt)
+    cu_q = torch.tensor([0] + list(itertools.accumulate(int(n) for n in lens_q)), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(itertools.accumulate(int(n) for n in lens_k)), dtype=torch.int32)
+    return q.to(device), k.to(device), v.to(device), cu_q.to(device), cu_k.to(device)
 
 
 @dataclasses.dataclass(frozen=True)

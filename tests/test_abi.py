@@ -319,3 +319,43 @@ def test_attn_decode_paged_rejects_bad_arguments(attn, kw, code):
                                 dict(b=0, q=0, kc=0, vc=0, table=0, lens=0, out=0)])
 def test_attn_decode_paged_empty_is_a_noop(attn, kw):
     assert _paged(attn, **kw) == 0
+
+
+def _varlen(attn, **kw):
+    from online_softmax_streaming_amd import _lib
+    g = 1 << 24
+    a = dict(q=1 * g, k=2 * g, v=3 * g, out=4 * g, cq=5 * g, ck=6 * g, b=3, h=4, hkv=2,
+             tq=300, tk=500, mq=200, d=64, causal=1, scale=0.125, dtype=2, m=None, l=None)
+    a.update(kw)
+    return _lib.lib().attn_fwd_varlen(a["q"], a["k"], a["v"], a["out"], a["cq"], a["ck"], a["b"],
+                                      a["h"], a["hkv"], a["tq"], a["tk"], a["mq"], a["d"],
+                                      a["causal"], a["scale"], a["dtype"], a["m"], a["l"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), 1),
+    (dict(causal=2), 1),
+    (dict(hkv=3), 1),
+    (dict(d=48), 2),
+    (dict(scale=0.0), 1),
+    (dict(tq=-1), 1),
+    (dict(mq=301), 1),                    # longer than total_q
+    (dict(q=0), 1),
+    (dict(cq=0), 1),
+    (dict(ck=0), 1),
+    (dict(k=0), 1),
+    (dict(q=(1 << 24) + 8), 1),           # misaligned
+    (dict(cq=5 * (1 << 24) + 2), 1),      # misaligned offsets
+    (dict(out=(1 << 24) + 64), 1),        # out overlaps Q
+    (dict(tk=1 << 24, hkv=2, d=64), 2),   # packed K above 4 GiB
+    (dict(tq=1 << 31), 1),
+])
+def test_attn_fwd_varlen_rejects_bad_arguments(attn, kw, code):
+    from online_softmax_streaming_amd import _lib
+    assert _varlen(attn, **kw) == code, _lib.lib().attn_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(b=0), dict(h=0), dict(tq=0, mq=0),
+                                dict(b=0, q=0, k=0, v=0, out=0, cq=0, ck=0)])
+def test_attn_fwd_varlen_empty_is_a_noop(attn, kw):
+    assert _varlen(attn, **kw) == 0

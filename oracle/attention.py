@@ -73,7 +73,7 @@ def visible_mask(nq, nk, causal, rows=None, window=0):
     return vis
 
 
-def attention_rows(q, k, v, causal, scale, rows=None, window=0):
+def attention_rows(q, k, v, causal, scale, rows=None, window=0, mask=None):
     """Two-pass FP64 attention for one head, on the query rows ``rows``.
 
     q: [Nq, D], k: [Nk, D], v: [Nk, Dv] arrays (upcast exactly to float64 by
@@ -81,7 +81,10 @@ def attention_rows(q, k, v, causal, scale, rows=None, window=0):
 
     Returns (out [R, Dv], m [R], l [R]) where (m, l) is the row's merge state
     in natural-log units: sum_j exp(s_j) = l * exp(m); (m, l) = (-inf, 0) and
-    out = 0 for a row with no visible key.  ``window`` as in visible_mask.
+    out = 0 for a row with no visible key.  ``window`` as in visible_mask;
+    ``mask`` (bool [Nq, Nk], optional) further hides every key where it is
+    False: an arbitrary mask, which the workshops page lists among the
+    attention contract's non-features ("Scope and contracts").
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -104,6 +107,8 @@ def attention_rows(q, k, v, causal, scale, rows=None, window=0):
         # Scores for these rows, materialised in FP64.
         s = scale * (q[r] @ k.T)
         vis = visible_mask(nq, nk, causal, r, window)
+        if mask is not None:
+            vis = vis & np.asarray(mask, dtype=bool)[r]
         s = np.where(vis, s, NEG_INF)
         nonempty = vis.any(axis=1)
 
@@ -125,9 +130,10 @@ def attention_rows(q, k, v, causal, scale, rows=None, window=0):
     return out, m_all, l_all
 
 
-def attention(q, k, v, causal, scale):
+def attention(q, k, v, causal, scale, window=0, mask=None):
     """Batched two-pass FP64 attention on [B, H, N, D] arrays.
 
+    ``mask``: optional bool array broadcastable to [B, H, Nq, Nk].
     Returns (out [B, H, Nq, Dv], m [B, H, Nq], l [B, H, Nq]).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -139,8 +145,12 @@ def attention(q, k, v, causal, scale):
     l = np.zeros((b, h, nq), dtype=np.float64)
     for bi in range(b):
         for hi in range(h):
+            mk = None
+            if mask is not None:
+                mk = np.broadcast_to(np.asarray(mask, dtype=bool),
+                                     (b, h, nq, k.shape[2]))[bi, hi]
             o, mm, ll = attention_rows(q[bi, hi], k[bi, hi], v[bi, hi],
-                                       causal, scale)
+                                       causal, scale, window=window, mask=mk)
             out[bi, hi], m[bi, hi], l[bi, hi] = o, mm, ll
     return out, m, l
 

@@ -175,6 +175,35 @@ ATTN_API int attn_bwd(const void* Q, const void* K, const void* V, const void* O
                       int64_t D, int causal, float scale, int dtype, void* stream);
 
 /*
+ * attn_fwd_masked -- attn_fwd_gqa with an arbitrary boolean mask and/or a
+ * sliding window (the arbitrary masks that [W] "Scope and contracts" lists
+ * as an extension opportunity; the per-row computation is [AK] row A3's).
+ *
+ * Key j is visible to query row i of head (b, h) iff the causal rule of
+ * attn_fwd holds (when causal == 1), the window holds (when window > 0:
+ * j > i + (Nk - Nq) - window, causal == 1 required), and, when mask is not
+ * NULL, bit (j % 32) of word mask[b*mask_stride_b + h*mask_stride_h +
+ * i*ceil(Nk/32) + j/32] is set.  Rows with no visible key get out = 0 and
+ * (m, l) = (-inf, 0).  A window skips the key tiles before each query
+ * tile's window.
+ *
+ * mask: NULL or a device array of uint32 words, 4-byte aligned, bit-packed
+ *   row by row ([B or 1, H or 1, Nq, ceil(Nk/32)] with strides in words;
+ *   a stride of 0 broadcasts over that dimension).  Bits past Nk in a row's
+ *   last word are ignored.  Values are not scanned.
+ * Other arguments, layout, errors and memory as attn_fwd_gqa (m_out, l_out
+ * may be NULL; window >= 0, mask strides >= 0); out, m_out and l_out must
+ * not overlap the mask.  Every Nq takes the tiled kernels (no split-key
+ * decode path), so the call allocates nothing.
+ */
+ATTN_API int attn_fwd_masked(const void* Q, const void* K, const void* V, void* out,
+                             const uint32_t* mask, int64_t mask_stride_b,
+                             int64_t mask_stride_h, int64_t B, int64_t H, int64_t Hkv,
+                             int64_t Nq, int64_t Nk, int64_t D, int causal, int64_t window,
+                             float scale, int dtype, float* m_out, float* l_out,
+                             void* stream);
+
+/*
  * attn_fwd_varlen -- attention over a batch of packed sequences of
  * different lengths (the padding lengths that [W] "Scope and contracts"
  * lists as an extension opportunity, in packed form; per sequence the

@@ -19,6 +19,7 @@ from .attn import (  # noqa: F401
     attn_decode_paged,
     attn_fwd,
     attn_fwd_gqa,
+    attn_fwd_masked,
     attn_fwd_raw,
     attn_fwd_stats,
     attn_fwd_varlen,
@@ -26,6 +27,7 @@ from .attn import (  # noqa: F401
     default_scale,
     online_merge,
     online_merge_batch,
+    pack_mask,
     softmax_rows,
     softmax_rows_scratch_bytes,
 )

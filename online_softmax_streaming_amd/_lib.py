@@ -36,6 +36,9 @@ SIGNATURES = {
     "attn_fwd_varlen": (ctypes.c_int, [_c_ptr] * 6 + [_c_i64] * 7 + [ctypes.c_int, ctypes.c_float,
                                                                      ctypes.c_int, _c_ptr, _c_ptr,
                                                                      _c_ptr]),
+    "attn_fwd_masked": (ctypes.c_int, [_c_ptr] * 5 + [_c_i64] * 8 + [ctypes.c_int, _c_i64,
+                                                                     ctypes.c_float, ctypes.c_int,
+                                                                     _c_ptr, _c_ptr, _c_ptr]),
     "online_merge": (ctypes.c_int, [ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                     ctypes.c_double, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_double)]),

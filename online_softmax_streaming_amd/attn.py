@@ -181,6 +181,69 @@ def attn_bwd(q, k, v, out, dout, m, l, causal=False, scale=None, dq=None, dk=Non
     return dq, dk, dv
 
 
+def pack_mask(mask):
+    """Bit-pack a bool tensor [..., Nq, Nk] into int32 words [..., Nq,
+    ceil(Nk/32)] (bit j % 32 of word j / 32), the layout attn_fwd_masked
+    reads.  Input marshalling only; runs where ``mask`` lives."""
+    if not isinstance(mask, torch.Tensor) or mask.dtype != torch.bool:
+        raise ValueError("mask must be a bool tensor")
+    nk = mask.shape[-1]
+    words = (nk + 31) // 32
+    pad = words * 32 - nk
+    m = torch.nn.functional.pad(mask.to(torch.int64), (0, pad))
+    m = m.reshape(*mask.shape[:-1], words, 32)
+    weights = torch.tensor([1 << i for i in range(32)], dtype=torch.int64, device=mask.device)
+    packed = (m * weights).sum(dim=-1)
+    return torch.where(packed >= 1 << 31, packed - (1 << 32), packed).to(torch.int32).contiguous()
+
+
+def attn_fwd_masked(q, k, v, mask=None, causal=False, window=0, scale=None, out=None,
+                    want_stats=False, stream=None):
+    """Attention with an arbitrary mask and/or a sliding window; returns
+    (out, m, l) (m, l None unless ``want_stats``).
+
+    q: [B, H, Nq, D]; k, v: [B, Hkv, Nk, D].  ``mask``: None, or packed
+    int32 words [Bm, Hm, Nq, ceil(Nk/32)] with Bm in {1, B} and Hm in {1, H}
+    (see pack_mask); a size-1 dimension broadcasts.  ``window`` > 0 keeps
+    the last ``window`` keys up to each row's diagonal (needs ``causal``).
+    """
+    _validate(q, k, v, grouped=True)
+    b, h, nq, d = q.shape
+    hkv, nk = k.shape[1], k.shape[2]
+    sb = sh = 0
+    if mask is not None:
+        words = (nk + 31) // 32
+        if (not isinstance(mask, torch.Tensor) or mask.dtype != torch.int32
+                or mask.device != q.device or not mask.is_contiguous() or mask.dim() != 4
+                or tuple(mask.shape[2:]) != (nq, words) or mask.shape[0] not in (1, b)
+                or mask.shape[1] not in (1, h)):
+            raise ValueError("mask must be contiguous int32 [B or 1, H or 1, Nq, ceil(Nk/32)] "
+                             "on q's device")
+        sh = nq * words if mask.shape[1] == h else 0
+        sb = mask.shape[1] * nq * words if mask.shape[0] == b else 0
+    if scale is None:
+        scale = default_scale(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor like q")
+    m = l = None
+    if want_stats:
+        m = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
+        l = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        sth = _stream_handle(stream, q.device)
+        rc = lib().attn_fwd_masked(
+            *(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out)),
+            ctypes.c_void_p(mask.data_ptr()) if mask is not None else None, sb, sh,
+            b, h, hkv, nq, nk, d, int(bool(causal)), int(window), float(scale), _DTYPES[q.dtype],
+            ctypes.c_void_p(m.data_ptr()) if want_stats else None,
+            ctypes.c_void_p(l.data_ptr()) if want_stats else None, sth)
+    _check(rc, "attn_fwd_masked")
+    return out, m, l
+
+
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, causal=False,
                     scale=None, out=None, want_stats=False, stream=None):
     """Attention over packed sequences of different lengths; returns

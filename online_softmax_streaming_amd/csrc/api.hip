@@ -60,7 +60,9 @@ void keep_pool_memory() {
 
 int run_attention(const void* Q, const void* K, const void* V, void* out, int64_t B, int64_t H,
                   int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
-                  int dtype, float* m_out, float* l_out, void* stream) {
+                  int dtype, float* m_out, float* l_out, void* stream,
+                  const uint32_t* mask = nullptr, int64_t mask_sb = 0, int64_t mask_sh = 0,
+                  int64_t window = 0) {
   g_last_error[0] = '\0';
   if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16)
     return fail(ATTN_E_INVALID, "dtype %d is not ATTN_F32, ATTN_F16 or ATTN_BF16", dtype);
@@ -79,6 +81,9 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
       Nq * D > kI32Max || Nk * D > kI32Max || B * H * Nq > kI32Max)
     return fail(ATTN_E_INVALID,
                 "sizes exceed the 32-bit per-head limits (B*H, Nq*D, Nk*D, B*H*Nq < 2^31)");
+  if (window < 0) return fail(ATTN_E_INVALID, "window must be >= 0, got %lld", (long long)window);
+  if (window > 0 && causal != 1) return fail(ATTN_E_INVALID, "a sliding window needs causal = 1");
+  if (mask_sb < 0 || mask_sh < 0) return fail(ATTN_E_INVALID, "mask strides must be >= 0");
   if (B == 0 || H == 0 || Nq == 0) return ATTN_OK;
 
   const int64_t elem = dtype == ATTN_F32 ? 4 : 2;
@@ -97,6 +102,17 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
   if (overlaps(m_out, sbytes, out, qbytes) || overlaps(l_out, sbytes, out, qbytes) ||
       overlaps(m_out, sbytes, l_out, sbytes))
     return fail(ATTN_E_INVALID, "m_out / l_out overlap out or each other");
+  if (mask) {
+    if (!aligned(mask, 4)) return fail(ATTN_E_INVALID, "mask must be 4-byte aligned");
+    const int64_t words = (Nk + 31) / 32;
+    if (mask_sb > INT64_MAX / 8 / (B + 1) || mask_sh > INT64_MAX / 8 / (H + 1) ||
+        Nq > INT64_MAX / 8 / (words + 1))
+      return fail(ATTN_E_INVALID, "mask extent overflows 64 bits");
+    const int64_t mbytes = 4 * ((B - 1) * mask_sb + (H - 1) * mask_sh + Nq * words);
+    if (overlaps(out, qbytes, mask, mbytes) || overlaps(m_out, sbytes, mask, mbytes) ||
+        overlaps(l_out, sbytes, mask, mbytes))
+      return fail(ATTN_E_INVALID, "out, m_out or l_out overlaps the mask");
+  }
 
   attn::Problem p;
   p.q = Q;
@@ -115,13 +131,17 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
   p.scale = scale;
   p.dtype = static_cast<attn::DType>(dtype);
   p.stream = static_cast<hipStream_t>(stream);
+  p.mask = mask;
+  p.mask_sb = mask_sb;
+  p.mask_sh = mask_sh;
+  p.window = window;
 
   hipError_t e;
   if (Nk == 0) {
     e = attn::launch_fill_empty(p);
     return e == hipSuccess ? ATTN_OK : hip_fail(e, "fill kernel launch");
   }
-  if (Nq <= attn::kDecodeMaxNq) {
+  if (Nq <= attn::kDecodeMaxNq && !mask && window == 0) {
     const attn::DecodePlan plan = attn::plan_decode(p);
     keep_pool_memory();
     void* scratch = nullptr;
@@ -173,6 +193,14 @@ int attn_fwd_gqa(const void* Q, const void* K, const void* V, void* out, int64_t
                  int dtype, float* m_out, float* l_out, void* stream) {
   return run_attention(Q, K, V, out, B, H, Hkv, Nq, Nk, D, causal, scale, dtype, m_out, l_out,
                        stream);
+}
+
+int attn_fwd_masked(const void* Q, const void* K, const void* V, void* out, const uint32_t* mask,
+                    int64_t mask_stride_b, int64_t mask_stride_h, int64_t B, int64_t H,
+                    int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, int64_t window,
+                    float scale, int dtype, float* m_out, float* l_out, void* stream) {
+  return run_attention(Q, K, V, out, B, H, Hkv, Nq, Nk, D, causal, scale, dtype, m_out, l_out,
+                       stream, mask, mask_stride_b, mask_stride_h, window);
 }
 
 int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,

@@ -36,6 +36,11 @@ struct Problem {
   const int* cu_q = nullptr;  // [B + 1]
   const int* cu_k = nullptr;  // [B + 1]
   int64_t total_q = 0, total_k = 0;
+  // Arbitrary mask (prefill kernels, batched layout): bit j % 32 of word
+  // j / 32 of row (b, h, i) at mask + b*mask_sb + h*mask_sh + i*ceil(Nk/32);
+  // with `window` > 0 the prefill kernels also apply the sliding window.
+  const uint32_t* mask = nullptr;
+  int64_t mask_sb = 0, mask_sh = 0;
 };
 
 // Streaming prefill on bf16/f16 matrix cores (prefill_mfma.hip).

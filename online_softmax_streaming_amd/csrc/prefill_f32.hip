@@ -35,13 +35,23 @@ struct F32Args {
   const int* cu_k;
   int H, Hkv;
   int total_q, total_k;
+  // Masked mode: optional bit-packed mask and sliding window, as in the
+  // matrix-core kernel.
+  const uint32_t* mask;
+  int64_t mask_sb, mask_sh;
+  int mask_words;
+  int window;
 };
+
+enum : int { kModeBatched = 0, kModeVarlen = 1, kModeMasked = 2 };
 
 constexpr int kThreads = 128;
 constexpr int kBNF = 32;
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
+  constexpr bool VARLEN = MODE == kModeVarlen;
+  constexpr bool MASKED = MODE == kModeMasked;
   constexpr int TPQ = D > 64 ? 2 : 1;
   constexpr int DT = D / TPQ;
   constexpr int QPB = kThreads / TPQ;
@@ -97,8 +107,15 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
   int kend = Nk;
   if (CAUSAL) kend = min(Nk, min(i0 + QPB, Nq) + off);
   const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  const int win = MASKED ? a.window : 0;
+  const int t_first = win > 0 ? max(0, i0 + off - win + 1) / BN : 0;
+  const uint32_t* mrow = nullptr;
+  if (MASKED && a.mask && qrow < Nq) {
+    const int b = bh / a.H, h = bh - b * a.H;
+    mrow = a.mask + (int64_t)b * a.mask_sb + (int64_t)h * a.mask_sh + (int64_t)qrow * a.mask_words;
+  }
 
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t_first; t < ntiles; ++t) {
     const int j0 = t * BN;
     // Stage the tile: 16-byte loads, rows past Nk zero.
     for (int e = tid; e < BN * D / 4; e += kThreads) {
@@ -114,6 +131,9 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
     }
     __syncthreads();
 
+    // The row's mask bits for keys j0 .. j0+31 (all set without a mask).
+    uint32_t mw = ~0u;
+    if (MASKED && a.mask) mw = mrow && j0 / 32 < a.mask_words ? mrow[j0 / 32] : 0u;
     float s[BN];
     float mx = kNegInf;
 #pragma unroll
@@ -123,7 +143,8 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
       for (int d = 0; d < DT; ++d) dot = __builtin_fmaf(q[d], Ks[jj * D + part * DT + d], dot);
       if (TPQ == 2) dot += __shfl_xor(dot, 1);
       const int j = j0 + jj;
-      const bool vis = j < Nk && (!CAUSAL || j <= qrow + off);
+      bool vis = j < Nk && (!CAUSAL || j <= qrow + off);
+      if (MASKED) vis = vis && (win <= 0 || j > qrow + off - win) && ((mw >> jj) & 1u);
       // Rounded product kept apart from the later subtraction, so the
       // largest score gives exactly 2^0 = 1.
       s[jj] = vis ? dot * c : kNegInf;
@@ -162,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, int MODE>
 hipError_t launch_typed(const Problem& p) {
   constexpr int TPQ = D > 64 ? 2 : 1;
   constexpr int QPB = kThreads / TPQ;
@@ -184,16 +205,24 @@ hipError_t launch_typed(const Problem& p) {
   a.Hkv = (int)p.Hkv;
   a.total_q = (int)p.total_q;
   a.total_k = (int)p.total_k;
+  a.mask = p.mask;
+  a.mask_sb = p.mask_sb;
+  a.mask_sh = p.mask_sh;
+  a.mask_words = (int)((p.Nk + 31) / 32);
+  a.window = (int)p.window;
   const int64_t grid = p.B * p.H * a.nqt;
-  hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL, MODE>), dim3((unsigned)grid), dim3(kThreads), 0,
                      p.stream, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const Problem& p) {
-  if (p.cu_q) return p.causal ? launch_typed<D, true, true>(p) : launch_typed<D, false, true>(p);
-  return p.causal ? launch_typed<D, true, false>(p) : launch_typed<D, false, false>(p);
+  if (p.cu_q)
+    return p.causal ? launch_typed<D, true, kModeVarlen>(p) : launch_typed<D, false, kModeVarlen>(p);
+  if (p.mask || p.window > 0)
+    return p.causal ? launch_typed<D, true, kModeMasked>(p) : launch_typed<D, false, kModeMasked>(p);
+  return p.causal ? launch_typed<D, true, kModeBatched>(p) : launch_typed<D, false, kModeBatched>(p);
 }
 
 }  // namespace

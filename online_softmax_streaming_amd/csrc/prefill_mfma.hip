@@ -75,7 +75,19 @@ struct PrefillArgs {
   const int* cu_k;
   int H, Hkv;
   int total_q, total_k;
+  // Masked mode (MASKED kernels only, batched layout): an optional
+  // bit-packed mask, bit j % 32 of word j / 32 of row (b, h, i) at
+  // mask + b*mask_sb + h*mask_sh + i*mask_words, and an optional sliding
+  // window (0 = none).
+  const uint32_t* mask;
+  int64_t mask_sb, mask_sh;
+  int mask_words;
+  int window;
 };
+
+// Kernel modes: batched [B, H, N, D]; packed variable-length sequences;
+// batched with an arbitrary mask and/or a sliding window.
+enum : int { kModeBatched = 0, kModeVarlen = 1, kModeMasked = 2 };
 
 constexpr int kBN = 64;              // keys per tile
 // LDS operand reads in flight ahead of the MFMA that uses them.
@@ -89,9 +101,11 @@ constexpr int kKPF = ATTN_KPF;
 constexpr int kVPF = ATTN_VPF;
 constexpr float kRefreshGap = 8.0f;  // base-2 units; see the file comment
 
-template <typename T, int D, int NW, bool CAUSAL, bool VARLEN>
+template <typename T, int D, int NW, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_mfma_kernel(PrefillArgs a) {
+  constexpr bool VARLEN = MODE == kModeVarlen;
+  constexpr bool MASKED = MODE == kModeMasked;
   typedef typename Mfma<T>::vec8 vec8;
   typedef typename Mfma<T>::vec4 vec4;
   typedef typename Mfma<T>::vec2 vec2;
@@ -184,9 +198,12 @@ void prefill_mfma_kernel(PrefillArgs a) {
                    : vec8{};
     }
 
-    // Key range that holds a visible key for some real row of this tile.
+    // Key range that holds a visible key for some real row of this tile
+    // (a window hides every key below row i0's lower bound from all rows).
     int kend = Nk;
     if (CAUSAL) kend = min(Nk, min(i0 + BM, Nq) + off);
+    const int win = MASKED ? a.window : 0;
+    const int t_first = win > 0 ? max(0, i0 + off - win + 1) / BN : 0;
     const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
 
     // Buffer resources over this head's K and V: offsets at or past Nk rows
@@ -261,7 +278,18 @@ void prefill_mfma_kernel(PrefillArgs a) {
       }
     };
 
-    auto compute = [&](auto bufc, int j0, bool need_mask) {
+    // Mask words of this lane's row for keys j0 .. j0+63 (MASKED only).
+    const uint32_t* mrow = nullptr;
+    if (MASKED && a.mask && qrow < Nq) {
+      const int b = bh / a.H, h = bh - b * a.H;
+      mrow = a.mask + (int64_t)b * a.mask_sb + (int64_t)h * a.mask_sh + (int64_t)qrow * a.mask_words;
+    }
+    auto mask_word = [&](int w) -> uint32_t {
+      if (!MASKED || !a.mask) return ~0u;
+      return mrow && w < a.mask_words ? mrow[w] : 0u;
+    };
+
+    auto compute = [&](auto bufc, int j0, bool need_mask, uint32_t mw0, uint32_t mw1) {
       constexpr int buf = decltype(bufc)::value;
       const unsigned char* kt = tile_ptr(buf, 0);
       const unsigned char* vt = tile_ptr(buf, 1);
@@ -308,12 +336,20 @@ void prefill_mfma_kernel(PrefillArgs a) {
       __builtin_amdgcn_sched_barrier(0);
 
       if (need_mask) {
+        // Register r of block mb holds key j0 + 32mb + 8(r/4) + 4*h32 + r%4,
+        // bit 8(r/4) + r%4 of the lane's mask word for block mb shifted by
+        // 4*h32.
+        const uint32_t mws[2] = {mw0 >> (4 * h32), mw1 >> (4 * h32)};
   #pragma unroll
         for (int mb = 0; mb < BN / 32; ++mb) {
   #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int j = j0 + mb * 32 + (r >> 2) * 8 + h32 * 4 + (r & 3);
-            const bool vis = j < Nk && (!CAUSAL || j <= qrow + off);
+            bool vis = j < Nk && (!CAUSAL || j <= qrow + off);
+            if (MASKED) {
+              vis = vis && (win <= 0 || j > qrow + off - win);
+              vis = vis && ((mws[mb] >> ((r >> 2) * 8 + (r & 3))) & 1u);
+            }
             s[mb][r] = vis ? s[mb][r] : kNegInf;
           }
         }
@@ -367,8 +403,8 @@ void prefill_mfma_kernel(PrefillArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    if (ntiles > 0) {
-      load_tile(0, 0);
+    if (ntiles > t_first) {
+      load_tile(t_first * BN, 0);
       __syncthreads();
       const int q_last = min(qw0 + 32, Nq) - 1;  // last real row of this wave
       auto step = [&](auto bufc, int t) {
@@ -376,15 +412,19 @@ void prefill_mfma_kernel(PrefillArgs a) {
         const int j0 = t * BN;
         const bool more = t + 1 < ntiles;
         if (more) load_tile(j0 + BN, buf ^ 1);  // in flight while this tile is computed
-        const bool active = qw0 < Nq && (!CAUSAL || j0 <= q_last + off);
+        // The mask words are requested before the tile's products.
+        const uint32_t mw0 = mask_word(j0 / 32), mw1 = mask_word(j0 / 32 + 1);
+        bool active = qw0 < Nq && (!CAUSAL || j0 <= q_last + off);
+        if (MASKED && win > 0) active = active && j0 + BN - 1 > qw0 + off - win;
         if (active) {
-          const bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + off);
-          compute(bufc, j0, need_mask);
+          bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + off);
+          if (MASKED) need_mask = need_mask || a.mask || (win > 0 && j0 <= q_last + off - win);
+          compute(bufc, j0, need_mask, mw0, mw1);
         }
         // Buffer buf^1 was last read in step t-1, before that step's barrier.
         __syncthreads();
       };
-      for (int t = 0; t < ntiles; t += 2) {
+      for (int t = t_first; t < ntiles; t += 2) {
         step(std::integral_constant<int, 0>{}, t);
         if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
       }
@@ -419,7 +459,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
   }  // pass
 }
 
-template <typename T, int D, int NW, bool CAUSAL, bool VARLEN>
+template <typename T, int D, int NW, bool CAUSAL, int MODE>
 hipError_t launch_typed(const Problem& p) {
   constexpr int BM = 32 * NW;
   PrefillArgs a;
@@ -439,13 +479,18 @@ hipError_t launch_typed(const Problem& p) {
   a.Hkv = (int)p.Hkv;
   a.total_q = (int)p.total_q;
   a.total_k = (int)p.total_k;
+  a.mask = p.mask;
+  a.mask_sb = p.mask_sb;
+  a.mask_sh = p.mask_sh;
+  a.mask_words = (int)((p.Nk + 31) / 32);
+  a.window = (int)p.window;
   a.nwork = CAUSAL ? (a.nqt + 1) / 2 : a.nqt;
   const int64_t total = p.B * p.H * a.nwork;
   a.total = (int)total;
   const int64_t grid = (total + 7) / 8 * 8;
   a.per_xcd = (int)(grid / 8);
   a.c = p.scale * kLog2e;
-  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, NW, CAUSAL, VARLEN>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, NW, CAUSAL, MODE>), dim3((unsigned)grid),
                      dim3(NW * 64), 0, p.stream, a);
   return hipGetLastError();
 }
@@ -459,10 +504,13 @@ constexpr int kWaves = ATTN_PREFILL_WAVES;
 template <typename T, int D>
 hipError_t launch_d(const Problem& p) {
   if (p.cu_q)
-    return p.causal ? launch_typed<T, D, kWaves, true, true>(p)
-                    : launch_typed<T, D, kWaves, false, true>(p);
-  return p.causal ? launch_typed<T, D, kWaves, true, false>(p)
-                  : launch_typed<T, D, kWaves, false, false>(p);
+    return p.causal ? launch_typed<T, D, kWaves, true, kModeVarlen>(p)
+                    : launch_typed<T, D, kWaves, false, kModeVarlen>(p);
+  if (p.mask || p.window > 0)
+    return p.causal ? launch_typed<T, D, kWaves, true, kModeMasked>(p)
+                    : launch_typed<T, D, kWaves, false, kModeMasked>(p);
+  return p.causal ? launch_typed<T, D, kWaves, true, kModeBatched>(p)
+                  : launch_typed<T, D, kWaves, false, kModeBatched>(p);
 }
 
 template <typename T>

@@ -359,3 +359,29 @@ def test_attn_fwd_varlen_rejects_bad_arguments(attn, kw, code):
                                 dict(b=0, q=0, k=0, v=0, out=0, cq=0, ck=0)])
 def test_attn_fwd_varlen_empty_is_a_noop(attn, kw):
     assert _varlen(attn, **kw) == 0
+
+
+def _masked(attn, **kw):
+    from online_softmax_streaming_amd import _lib
+    g = 1 << 24
+    a = dict(q=1 * g, k=2 * g, v=3 * g, out=4 * g, mask=5 * g, sb=0, sh=0, b=2, h=4, hkv=2,
+             nq=64, nk=64, d=64, causal=1, window=0, scale=0.125, dtype=2)
+    a.update(kw)
+    return _lib.lib().attn_fwd_masked(a["q"], a["k"], a["v"], a["out"], a["mask"], a["sb"], a["sh"],
+                                      a["b"], a["h"], a["hkv"], a["nq"], a["nk"], a["d"],
+                                      a["causal"], a["window"], a["scale"], a["dtype"], None, None,
+                                      None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=-1), 1),
+    (dict(window=8, causal=0), 1),
+    (dict(sb=-1), 1),
+    (dict(mask=5 * (1 << 24) + 2), 1),          # misaligned mask
+    (dict(out=5 * (1 << 24)), 1),               # out overlaps the mask
+    (dict(d=48), 2),
+    (dict(hkv=3), 1),
+])
+def test_attn_fwd_masked_rejects_bad_arguments(attn, kw, code):
+    from online_softmax_streaming_amd import _lib
+    assert _masked(attn, **kw) == code, _lib.lib().attn_last_error()

@@ -405,6 +405,8 @@ void prefill_mfma_kernel(PrefillArgs a) {
 
     if (ntiles > t_first) {
       load_tile(t_first * BN, 0);
+      // Mask words of the next tile, fetched one tile ahead.
+      uint32_t nw0 = mask_word(2 * t_first), nw1 = mask_word(2 * t_first + 1);
       __syncthreads();
       const int q_last = min(qw0 + 32, Nq) - 1;  // last real row of this wave
       auto step = [&](auto bufc, int t) {
@@ -412,10 +414,15 @@ void prefill_mfma_kernel(PrefillArgs a) {
         const int j0 = t * BN;
         const bool more = t + 1 < ntiles;
         if (more) load_tile(j0 + BN, buf ^ 1);  // in flight while this tile is computed
-        // The mask words are requested before the tile's products.
-        const uint32_t mw0 = mask_word(j0 / 32), mw1 = mask_word(j0 / 32 + 1);
+        const uint32_t mw0 = nw0, mw1 = nw1;
+        if (MASKED && more) {
+          nw0 = mask_word(j0 / 32 + 2);
+          nw1 = mask_word(j0 / 32 + 3);
+        }
         bool active = qw0 < Nq && (!CAUSAL || j0 <= q_last + off);
         if (MASKED && win > 0) active = active && j0 + BN - 1 > qw0 + off - win;
+        // A tile none of this wave's rows may see under the mask is skipped.
+        if (MASKED && a.mask) active = active && __builtin_amdgcn_ballot_w64((mw0 | mw1) != 0u) != 0;
         if (active) {
           bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + off);
           if (MASKED) need_mask = need_mask || a.mask || (win > 0 && j0 <= q_last + off - win);

@@ -168,6 +168,25 @@ def make_varlen(lens_q, lens_k, H, Hkv, D, dtype, seed=0, device="cpu"):
     return q.to(device), k.to(device), v.to(device), cu_q.to(device), cu_k.to(device)
 
 
+def varlen_lengths(n_seq, lo, hi, seed=0):
+    """Seeded sequence lengths, uniform in [lo, hi] (a mixed-length batch)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return [int(x) for x in torch.randint(lo, hi + 1, (n_seq,), generator=g)]
+
+
+def causal_pairs(nq, nk, window=0):
+    """Visible (query, key) pairs of one causal head, keys aligned to the
+    end of the query block, with an optional sliding window."""
+    off = nk - nq
+    total = 0
+    for i in range(nq):
+        hi = min(nk - 1, i + off)
+        lo = 0 if window <= 0 else max(0, i + off - window + 1)
+        total += max(0, hi - lo + 1)
+    return total
+
+
 @dataclasses.dataclass(frozen=True)
 class SoftmaxWorkload:
     """A wide-row softmax input: x ~ 3 * N(0, 1) float32, rounded to dtype."""

@@ -41,6 +41,7 @@ from .softmax import (  # noqa: F401
 )
 from .paged import attention_paged, gather_pages  # noqa: F401
 from .varlen import attention_varlen  # noqa: F401
+from .dropout import attention_dropout, keep_mask, philox4x64, threshold  # noqa: F401
 from .attention_backward import (  # noqa: F401
     attention_backward,
     attention_backward_head,

@@ -204,6 +204,32 @@ ATTN_API int attn_fwd_masked(const void* Q, const void* K, const void* V, void* 
                              void* stream);
 
 /*
+ * attn_fwd_dropout -- attn_fwd_gqa with dropout on the attention
+ * probabilities (dropout is one of the extension opportunities [W] "Scope
+ * and contracts" lists; the per-row computation is [AK] row A3's).
+ *
+ * With w_ij = exp(scale q_i.k_j - m_i) on visible keys and l_i = sum_j w_ij
+ * (dropout does not change m, l):
+ *     out_i = sum_j w_ij keep_ij V_j / l_i * 65536 / (65536 - T)
+ * keep_ij: 16-bit field j % 16 of Philox4x64-10 (Salmon et al., SC 2011) on
+ * counter (j / 16, i, b*H + h, offset) under key (seed, 0) is >= T, field t
+ * at bits 16*(t % 4) of output word t / 4; T = round(p * 65536), so the
+ * drop probability is T / 65536 and the output is unbiased.  Query row i
+ * and key j are indices within the head.  The same (seed, offset) gives the
+ * same mask on every call; advance `offset` between calls for fresh masks.
+ *
+ * p: 0 <= p < 1 and round(p * 65536) <= 65535 (else ATTN_E_INVALID); p = 0
+ * gives attn_fwd_gqa's output bit for bit.  Other arguments, layout,
+ * errors as attn_fwd_gqa; m_out, l_out may be NULL.  Every Nq takes the
+ * tiled kernels; the call allocates nothing.
+ */
+ATTN_API int attn_fwd_dropout(const void* Q, const void* K, const void* V, void* out,
+                              int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk,
+                              int64_t D, int causal, float scale, float p, uint64_t seed,
+                              uint64_t offset, int dtype, float* m_out, float* l_out,
+                              void* stream);
+
+/*
  * attn_fwd_varlen -- attention over a batch of packed sequences of
  * different lengths (the padding lengths that [W] "Scope and contracts"
  * lists as an extension opportunity, in packed form; per sequence the

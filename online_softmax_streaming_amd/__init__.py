@@ -18,6 +18,7 @@ from .attn import (  # noqa: F401
     attn_bwd,
     attn_decode_paged,
     attn_fwd,
+    attn_fwd_dropout,
     attn_fwd_gqa,
     attn_fwd_masked,
     attn_fwd_raw,

@@ -39,6 +39,10 @@ SIGNATURES = {
     "attn_fwd_masked": (ctypes.c_int, [_c_ptr] * 5 + [_c_i64] * 8 + [ctypes.c_int, _c_i64,
                                                                      ctypes.c_float, ctypes.c_int,
                                                                      _c_ptr, _c_ptr, _c_ptr]),
+    "attn_fwd_dropout": (ctypes.c_int, [_c_ptr] * 4 + [_c_i64] * 6 + [ctypes.c_int, ctypes.c_float,
+                                                                      ctypes.c_float, ctypes.c_uint64,
+                                                                      ctypes.c_uint64, ctypes.c_int,
+                                                                      _c_ptr, _c_ptr, _c_ptr]),
     "online_merge": (ctypes.c_int, [ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                     ctypes.c_double, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_double)]),

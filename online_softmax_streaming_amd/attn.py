@@ -244,6 +244,37 @@ def attn_fwd_masked(q, k, v, mask=None, causal=False, window=0, scale=None, out=
     return out, m, l
 
 
+def attn_fwd_dropout(q, k, v, p, seed, offset=0, causal=False, scale=None, out=None,
+                     want_stats=False, stream=None):
+    """Attention with dropout on the probabilities (Philox4x64-10 keep mask,
+    kept weights scaled by 65536 / (65536 - round(p * 65536))); returns
+    (out, m, l) (m, l None unless ``want_stats``).  q: [B, H, Nq, D];
+    k, v: [B, Hkv, Nk, D]."""
+    _validate(q, k, v, grouped=True)
+    b, h, nq, d = q.shape
+    hkv, nk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = default_scale(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor like q")
+    m = l = None
+    if want_stats:
+        m = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
+        l = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        sth = _stream_handle(stream, q.device)
+        rc = lib().attn_fwd_dropout(
+            *(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out)), b, h, hkv, nq, nk, d,
+            int(bool(causal)), float(scale), float(p), int(seed), int(offset), _DTYPES[q.dtype],
+            ctypes.c_void_p(m.data_ptr()) if want_stats else None,
+            ctypes.c_void_p(l.data_ptr()) if want_stats else None, sth)
+    _check(rc, "attn_fwd_dropout")
+    return out, m, l
+
+
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, causal=False,
                     scale=None, out=None, want_stats=False, stream=None):
     """Attention over packed sequences of different lengths; returns

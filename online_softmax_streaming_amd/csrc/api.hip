@@ -62,7 +62,7 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
                   int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
                   int dtype, float* m_out, float* l_out, void* stream,
                   const uint32_t* mask = nullptr, int64_t mask_sb = 0, int64_t mask_sh = 0,
-                  int64_t window = 0) {
+                  int64_t window = 0, const attn::Problem* dropout = nullptr) {
   g_last_error[0] = '\0';
   if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16)
     return fail(ATTN_E_INVALID, "dtype %d is not ATTN_F32, ATTN_F16 or ATTN_BF16", dtype);
@@ -135,13 +135,19 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
   p.mask_sb = mask_sb;
   p.mask_sh = mask_sh;
   p.window = window;
+  if (dropout) {
+    p.dropout = true;
+    p.seed = dropout->seed;
+    p.offset = dropout->offset;
+    p.drop_t = dropout->drop_t;
+  }
 
   hipError_t e;
   if (Nk == 0) {
     e = attn::launch_fill_empty(p);
     return e == hipSuccess ? ATTN_OK : hip_fail(e, "fill kernel launch");
   }
-  if (Nq <= attn::kDecodeMaxNq && !mask && window == 0) {
+  if (Nq <= attn::kDecodeMaxNq && !mask && window == 0 && !dropout) {
     const attn::DecodePlan plan = attn::plan_decode(p);
     keep_pool_memory();
     void* scratch = nullptr;
@@ -201,6 +207,25 @@ int attn_fwd_masked(const void* Q, const void* K, const void* V, void* out, cons
                     float scale, int dtype, float* m_out, float* l_out, void* stream) {
   return run_attention(Q, K, V, out, B, H, Hkv, Nq, Nk, D, causal, scale, dtype, m_out, l_out,
                        stream, mask, mask_stride_b, mask_stride_h, window);
+}
+
+int attn_fwd_dropout(const void* Q, const void* K, const void* V, void* out, int64_t B, int64_t H,
+                     int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
+                     float p, uint64_t seed, uint64_t offset, int dtype, float* m_out,
+                     float* l_out, void* stream) {
+  g_last_error[0] = '\0';
+  if (!(p >= 0.f) || !(p < 1.f))
+    return fail(ATTN_E_INVALID, "dropout p must satisfy 0 <= p < 1, got %g", (double)p);
+  const double t = floor((double)p * 65536.0 + 0.5);
+  if (t > 65535.0)
+    return fail(ATTN_E_INVALID, "dropout p=%g rounds to a threshold of 65536 (drop everything)",
+                (double)p);
+  attn::Problem d;
+  d.seed = seed;
+  d.offset = offset;
+  d.drop_t = (uint32_t)t;
+  return run_attention(Q, K, V, out, B, H, Hkv, Nq, Nk, D, causal, scale, dtype, m_out, l_out,
+                       stream, nullptr, 0, 0, 0, &d);
 }
 
 int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,

@@ -41,6 +41,12 @@ struct Problem {
   // with `window` > 0 the prefill kernels also apply the sliding window.
   const uint32_t* mask = nullptr;
   int64_t mask_sb = 0, mask_sh = 0;
+  // Dropout on the probabilities (prefill kernels, batched layout): keep
+  // key j of row i of head bh iff 16-bit field j % 16 of Philox4x64-10 on
+  // counter (j / 16, i, bh, offset), key (seed, 0), is >= drop_t.
+  bool dropout = false;
+  uint64_t seed = 0, offset = 0;
+  uint32_t drop_t = 0;
 };
 
 // Streaming prefill on bf16/f16 matrix cores (prefill_mfma.hip).

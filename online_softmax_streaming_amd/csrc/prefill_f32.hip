@@ -41,9 +41,13 @@ struct F32Args {
   int64_t mask_sb, mask_sh;
   int mask_words;
   int window;
+  // Dropout mode, as in the matrix-core kernel.
+  uint64_t seed, offset;
+  uint32_t drop_t;
+  float keep_gain;
 };
 
-enum : int { kModeBatched = 0, kModeVarlen = 1, kModeMasked = 2 };
+enum : int { kModeBatched = 0, kModeVarlen = 1, kModeMasked = 2, kModeDropout = 3 };
 
 constexpr int kThreads = 128;
 constexpr int kBNF = 32;
@@ -52,6 +56,7 @@ template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
   constexpr bool VARLEN = MODE == kModeVarlen;
   constexpr bool MASKED = MODE == kModeMasked;
+  constexpr bool DROPOUT = MODE == kModeDropout;
   constexpr int TPQ = D > 64 ? 2 : 1;
   constexpr int DT = D / TPQ;
   constexpr int QPB = kThreads / TPQ;
@@ -160,6 +165,20 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
       rs += s[jj];
     }
     l_run = l_run * alpha + rs;
+    if (DROPOUT) {
+      // Keys j0 .. j0+31 are fields of Philox blocks j0/16 and j0/16 + 1 of
+      // this row (counter (j / 16, i, bh, offset), key (seed, 0)).
+#pragma unroll
+      for (int blk = 0; blk < BN / 16; ++blk) {
+        uint64_t w[4] = {(uint64_t)((j0 >> 4) + blk), (uint64_t)qrow, (uint64_t)bh, a.offset};
+        philox4x64_10(w, a.seed, 0);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const uint32_t field = (uint32_t)(w[t >> 2] >> (16 * (t & 3))) & 0xFFFFu;
+          if (field < a.drop_t) s[16 * blk + t] = 0.f;
+        }
+      }
+    }
 #pragma unroll
     for (int d = 0; d < DT; ++d) {
       float x = acc[d] * alpha;
@@ -172,7 +191,8 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
   }
 
   if (qrow < Nq) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    if (DROPOUT) inv *= a.keep_gain;
 #pragma unroll
     for (int d = 0; d < DT; ++d) Oh[(int64_t)qrow * sq + part * DT + d] = acc[d] * inv;
     if (part == 0) {
@@ -210,6 +230,10 @@ hipError_t launch_typed(const Problem& p) {
   a.mask_sh = p.mask_sh;
   a.mask_words = (int)((p.Nk + 31) / 32);
   a.window = (int)p.window;
+  a.seed = p.seed;
+  a.offset = p.offset;
+  a.drop_t = p.drop_t;
+  a.keep_gain = (float)(65536.0 / (65536.0 - (double)p.drop_t));
   const int64_t grid = p.B * p.H * a.nqt;
   hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL, MODE>), dim3((unsigned)grid), dim3(kThreads), 0,
                      p.stream, a);
@@ -222,6 +246,8 @@ hipError_t launch_d(const Problem& p) {
     return p.causal ? launch_typed<D, true, kModeVarlen>(p) : launch_typed<D, false, kModeVarlen>(p);
   if (p.mask || p.window > 0)
     return p.causal ? launch_typed<D, true, kModeMasked>(p) : launch_typed<D, false, kModeMasked>(p);
+  if (p.dropout)
+    return p.causal ? launch_typed<D, true, kModeDropout>(p) : launch_typed<D, false, kModeDropout>(p);
   return p.causal ? launch_typed<D, true, kModeBatched>(p) : launch_typed<D, false, kModeBatched>(p);
 }
 

@@ -83,11 +83,18 @@ struct PrefillArgs {
   int64_t mask_sb, mask_sh;
   int mask_words;
   int window;
+  // Dropout mode: key j of row i of head bh is kept iff 16-bit field j % 16
+  // of Philox4x64-10 on counter (j / 16, i, bh, offset) under key (seed, 0)
+  // is >= drop_t; kept weights are scaled by keep_gain = 65536/(65536 - T).
+  uint64_t seed, offset;
+  uint32_t drop_t;
+  float keep_gain;
 };
 
 // Kernel modes: batched [B, H, N, D]; packed variable-length sequences;
-// batched with an arbitrary mask and/or a sliding window.
-enum : int { kModeBatched = 0, kModeVarlen = 1, kModeMasked = 2 };
+// batched with an arbitrary mask and/or a sliding window; batched with
+// dropout on the probabilities.
+enum : int { kModeBatched = 0, kModeVarlen = 1, kModeMasked = 2, kModeDropout = 3 };
 
 constexpr int kBN = 64;              // keys per tile
 // LDS operand reads in flight ahead of the MFMA that uses them.
@@ -106,6 +113,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_mfma_kernel(PrefillArgs a) {
   constexpr bool VARLEN = MODE == kModeVarlen;
   constexpr bool MASKED = MODE == kModeMasked;
+  constexpr bool DROPOUT = MODE == kModeDropout;
   typedef typename Mfma<T>::vec8 vec8;
   typedef typename Mfma<T>::vec4 vec4;
   typedef typename Mfma<T>::vec2 vec2;
@@ -392,6 +400,52 @@ void prefill_mfma_kernel(PrefillArgs a) {
       }
       l_run += rs;
 
+      if (DROPOUT) {
+        // Group c2 of pf holds keys j0 + 16c2 + t with t = 4*h32 + e%4 +
+        // 8*(e/4): fields t of Philox block ((j0 / 16) + c2, qrow, bh,
+        // offset), i.e. words h32 and h32 + 2 of it.  The two lanes of a row
+        // (h32 = 0, 1) each run two of the four blocks (groups 2*h32,
+        // 2*h32 + 1) and swap the two words the other lane needs.
+        uint64_t own[2][4];
+  #pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          own[cc][0] = (uint64_t)((j0 >> 4) + 2 * h32 + cc);
+          own[cc][1] = (uint64_t)qrow;
+          own[cc][2] = (uint64_t)bh;
+          own[cc][3] = a.offset;
+          philox4x64_10(own[cc], a.seed, 0);
+        }
+        uint64_t recv[2][2];
+  #pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+  #pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const uint64_t send = h32 ? own[cc][2 * x] : own[cc][2 * x + 1];  // word (1-h32) + 2x
+            uint32_t halves[2];
+  #pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              const uint32_t v32 = (uint32_t)(send >> (32 * hf));
+              const auto r = __builtin_amdgcn_permlane32_swap(v32, v32, false, false);
+              halves[hf] = h32 ? r[0] : r[1];  // the value of lane l ^ 32
+            }
+            recv[cc][x] = (uint64_t)halves[0] | ((uint64_t)halves[1] << 32);
+          }
+        }
+        const vec8 zero8 = vec8{};
+  #pragma unroll
+        for (int c2 = 0; c2 < BN / 16; ++c2) {
+          const bool mine = (c2 >> 1) == h32;
+          const uint64_t w_lo = mine ? (h32 ? own[c2 & 1][1] : own[c2 & 1][0]) : recv[c2 & 1][0];
+          const uint64_t w_hi = mine ? (h32 ? own[c2 & 1][3] : own[c2 & 1][2]) : recv[c2 & 1][1];
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint64_t w = e < 4 ? w_lo : w_hi;
+            const uint32_t field = (uint32_t)(w >> (16 * (e & 3))) & 0xFFFFu;
+            pf[c2][e] = field >= a.drop_t ? pf[c2][e] : zero8[e];
+          }
+        }
+      }
+
       // O^T += V^T P^T, each V^T operand read kVPF MFMAs ahead.
       __builtin_amdgcn_sched_barrier(0);
   #pragma unroll
@@ -440,7 +494,8 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // Epilogue: join the two half-wave sums, normalise, one cast, store.
     const float l_tot = half_sum(l_run);
     if (qrow < Nq) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      if (DROPOUT) inv *= a.keep_gain;
       T* orow = Oh + (int64_t)qrow * sq;
   #pragma unroll
       for (int n = 0; n < NB; ++n) {
@@ -491,6 +546,10 @@ hipError_t launch_typed(const Problem& p) {
   a.mask_sh = p.mask_sh;
   a.mask_words = (int)((p.Nk + 31) / 32);
   a.window = (int)p.window;
+  a.seed = p.seed;
+  a.offset = p.offset;
+  a.drop_t = p.drop_t;
+  a.keep_gain = (float)(65536.0 / (65536.0 - (double)p.drop_t));
   a.nwork = CAUSAL ? (a.nqt + 1) / 2 : a.nqt;
   const int64_t total = p.B * p.H * a.nwork;
   a.total = (int)total;
@@ -516,6 +575,9 @@ hipError_t launch_d(const Problem& p) {
   if (p.mask || p.window > 0)
     return p.causal ? launch_typed<T, D, kWaves, true, kModeMasked>(p)
                     : launch_typed<T, D, kWaves, false, kModeMasked>(p);
+  if (p.dropout)
+    return p.causal ? launch_typed<T, D, kWaves, true, kModeDropout>(p)
+                    : launch_typed<T, D, kWaves, false, kModeDropout>(p);
   return p.causal ? launch_typed<T, D, kWaves, true, kModeBatched>(p)
                   : launch_typed<T, D, kWaves, false, kModeBatched>(p);
 }

@@ -385,3 +385,12 @@ def _masked(attn, **kw):
 def test_attn_fwd_masked_rejects_bad_arguments(attn, kw, code):
     from online_softmax_streaming_amd import _lib
     assert _masked(attn, **kw) == code, _lib.lib().attn_last_error()
+
+
+@pytest.mark.parametrize("p", [-0.1, 1.0, float("nan"), 0.999995])
+def test_attn_fwd_dropout_rejects_bad_p(attn, p):
+    from online_softmax_streaming_amd import _lib
+    g = 1 << 24
+    rc = _lib.lib().attn_fwd_dropout(g, 2 * g, 3 * g, 4 * g, 1, 2, 2, 64, 64, 64, 0, 0.125, p, 1, 0,
+                                     2, None, None, None)
+    assert rc == 1, _lib.lib().attn_last_error()

@@ -344,18 +344,22 @@ void prefill_mfma_kernel(PrefillArgs a) {
       __builtin_amdgcn_sched_barrier(0);
 
       if (need_mask) {
-        // Register r of block mb holds key j0 + 32mb + 8(r/4) + 4*h32 + r%4,
-        // bit 8(r/4) + r%4 of the lane's mask word for block mb shifted by
-        // 4*h32.
+        // Register r of block mb holds key j0 + 4*h32 + kr with the
+        // immediate kr = 32mb + 8(r/4) + r%4; the ragged end and the causal
+        // rule become one per-lane limit (visible iff kr < lim), so each test
+        // compares an immediate.  The mask word bit of the key is bit
+        // 8(r/4) + r%4 of the lane's word for block mb shifted by 4*h32.
+        const int lim = min(Nk - j0, CAUSAL ? qrow + off - j0 + 1 : Nk - j0) - 4 * h32;
+        const int wlo = win > 0 ? qrow + off - win - j0 - 4 * h32 : -(1 << 30);  // visible iff kr > wlo
         const uint32_t mws[2] = {mw0 >> (4 * h32), mw1 >> (4 * h32)};
   #pragma unroll
         for (int mb = 0; mb < BN / 32; ++mb) {
   #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int j = j0 + mb * 32 + (r >> 2) * 8 + h32 * 4 + (r & 3);
-            bool vis = j < Nk && (!CAUSAL || j <= qrow + off);
+            const int kr = mb * 32 + (r >> 2) * 8 + (r & 3);
+            bool vis = kr < lim;
             if (MASKED) {
-              vis = vis && (win <= 0 || j > qrow + off - win);
+              vis = vis && kr > wlo;
               vis = vis && ((mws[mb] >> ((r >> 2) * 8 + (r & 3))) & 1u);
             }
             s[mb][r] = vis ? s[mb][r] : kNegInf;

@@ -7,6 +7,9 @@ sampled rows (first/last rows, tile edges, the ragged tail, random rows) of
 sampled heads, in the same launch configuration the benchmark times.
 Index work (causal visibility) is checked bit-exactly through the row state:
 with Q = 0 every visible score is 0, so m = 0 and l = #visible exactly.
+With $ATTN_PARITY_LOG set, every comparison appends its max abs error beside
+the output-rounding floor (what an exact kernel would still show after the
+one cast to the output type), so kernel error and rounding can be told apart.
 """
 
 import json
@@ -39,12 +42,27 @@ def _say(msg):
     print(f"[parity] {msg}", file=sys.stderr, flush=True)
 
 
+_LAST_FLOOR = [0.0]
+
+
+def _floor(want, dtype):
+    """Output-rounding floor: max |round(o) - o| over the oracle outputs o, the
+    error a kernel that computed o exactly would still show after the one
+    cast to the output type."""
+    if want.size == 0:
+        return 0.0
+    t = torch.from_numpy(np.ascontiguousarray(want))
+    return float((t.to(dtype).double() - t).abs().max())
+
+
 def _record(what, err, tol):
-    """Append the measured error to $ATTN_PARITY_LOG (JSON lines), if set."""
+    """Append the measured error and the rounding floor of the same
+    comparison to $ATTN_PARITY_LOG (JSON lines), if set."""
     path = os.environ.get("ATTN_PARITY_LOG")
     if path:
         with open(path, "a") as f:
-            f.write(json.dumps({"case": what, "max_abs_err": float(err), "tol": tol}) + "\n")
+            f.write(json.dumps({"case": what, "max_abs_err": float(err), "tol": tol,
+                                "rounding_floor": _LAST_FLOOR[0]}) + "\n")
 
 
 def _np(t):
@@ -57,7 +75,8 @@ def _compare_full(q, k, v, causal, scale, out, tol, m=None, l=None):
     got = _np(out)
     assert np.all(np.isfinite(got)), "non-finite output"
     err = np.max(np.abs(got - want)) if got.size else 0.0
-    assert err <= tol, f"max abs err {err} > {tol}"
+    _LAST_FLOOR[0] = _floor(want, out.dtype)
+    assert err <= tol, f"max abs err {err} > {tol} (rounding floor {_LAST_FLOOR[0]:.3g})"
     if m is not None:
         gm, gl = _np(m), _np(l)
         empty = wl == 0
@@ -79,6 +98,7 @@ def _sample_rows(nq, rng, extra=24):
 
 def _compare_sampled(q, k, v, causal, scale, out, tol, heads, rng):
     worst = 0.0
+    _LAST_FLOOR[0] = 0.0
     for b, h in heads:
         rows = _sample_rows(q.shape[2], rng)
         want, _, _ = oracle.attention_rows(_np(q[b, h]), _np(k[b, h]), _np(v[b, h]), causal,
@@ -86,7 +106,9 @@ def _compare_sampled(q, k, v, causal, scale, out, tol, heads, rng):
         got = _np(out[b, h, torch.as_tensor(rows, device=out.device)])
         assert np.all(np.isfinite(got))
         err = np.max(np.abs(got - want))
-        assert err <= tol, f"head ({b},{h}) max abs err {err} > {tol}"
+        _LAST_FLOOR[0] = max(_LAST_FLOOR[0], _floor(want, out.dtype))
+        assert err <= tol, (f"head ({b},{h}) max abs err {err} > {tol} "
+                            f"(rounding floor {_LAST_FLOOR[0]:.3g})")
         worst = max(worst, err)
     return worst
 
@@ -199,9 +221,11 @@ def test_decode_workload_sampled():
     heads = {(0, 0), (w.B - 1, w.H - 1)}
     heads |= {(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(6)}
     worst = 0.0
+    _LAST_FLOOR[0] = 0.0
     for b, h in sorted(heads):
         want = oracle.attention_rows(_np(q[b, h]), _np(k[b, h]), _np(v[b, h]), False, scale)[0]
         err = np.max(np.abs(_np(out[b, h]) - want))
+        _LAST_FLOOR[0] = max(_LAST_FLOOR[0], _floor(want, out.dtype))
         assert err <= TOL["bf16"], f"head ({b},{h}) err {err}"
         worst = max(worst, err)
     _record("decode_bf16 (sampled heads)", worst, TOL["bf16"])

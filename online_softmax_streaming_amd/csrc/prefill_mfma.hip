@@ -570,6 +570,7 @@ hipError_t launch_typed(const Problem& p) {
 #define ATTN_PREFILL_WAVES 8
 #endif
 constexpr int kWaves = ATTN_PREFILL_WAVES;
+constexpr int64_t kSmallGridWgs = 128;  // half of the 256 CUs
 
 template <typename T, int D>
 hipError_t launch_d(const Problem& p) {
@@ -582,6 +583,15 @@ hipError_t launch_d(const Problem& p) {
   if (p.dropout)
     return p.causal ? launch_typed<T, D, kWaves, true, kModeDropout>(p)
                     : launch_typed<T, D, kWaves, false, kModeDropout>(p);
+  // A small problem (fewer workgroups of kWaves waves than half the CUs)
+  // runs in two-wave workgroups: each wave's rows still stream every key, but
+  // four times as many workgroups spread over the CUs and each wave gets its
+  // SIMD alone, so the longest row block finishes sooner.
+  const int64_t nqt = (p.Nq + 32 * kWaves - 1) / (32 * kWaves);
+  const int64_t wgs = p.B * p.H * (p.causal ? (nqt + 1) / 2 : nqt);
+  if (wgs < kSmallGridWgs)
+    return p.causal ? launch_typed<T, D, 2, true, kModeBatched>(p)
+                    : launch_typed<T, D, 2, false, kModeBatched>(p);
   return p.causal ? launch_typed<T, D, kWaves, true, kModeBatched>(p)
                   : launch_typed<T, D, kWaves, false, kModeBatched>(p);
 }

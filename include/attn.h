@@ -146,11 +146,12 @@ ATTN_API int attn_fwd_gqa(const void* Q, const void* K, const void* V, void* out
  * Layout: Q, O, dO, dQ contiguous [B, H, Nq, D]; K, V, dK, dV contiguous
  * [B, Hkv, Nk, D]; m, l FP32 [B, H, Nq] exactly as attn_fwd_stats /
  * attn_fwd_gqa write them (O too: the forward's rounded output).  All
- * tensors but m, l use `dtype`, which must be ATTN_F16 or ATTN_BF16
- * (ATTN_F32 returns ATTN_E_UNSUPPORTED).  Arithmetic: Q K^T, dO V^T and every
- * sum in FP32 on bf16/f16 matrix cores; P and dS are rounded to `dtype` as
- * operands of the products that form dV, dK and dQ; one round-to-nearest-
- * even cast per output element.  No atomics: results are bitwise
+ * tensors but m, l use `dtype` (ATTN_F32, ATTN_F16 or ATTN_BF16).
+ * Arithmetic: for F16/BF16, Q K^T, dO V^T and every sum in FP32 on bf16/f16
+ * matrix cores; P and dS are rounded to `dtype` as operands of the products
+ * that form dV, dK and dQ; one round-to-nearest-even cast per output
+ * element.  For F32, everything in FP32 on the vector ALUs with nothing
+ * rounded to a narrower type.  No atomics: results are bitwise
  * reproducible from run to run.
  *
  * Arguments:

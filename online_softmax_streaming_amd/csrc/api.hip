@@ -244,8 +244,6 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
   if (D <= 0) return fail(ATTN_E_INVALID, "D must be positive, got %lld", (long long)D);
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(ATTN_E_INVALID, "scale must be finite and > 0, got %g", (double)scale);
-  if (dtype == ATTN_F32)
-    return fail(ATTN_E_UNSUPPORTED, "attn_bwd: FP32 inputs not built (F16 and BF16 are)");
   if (D != 16 && D != 32 && D != 64 && D != 128)
     return fail(ATTN_E_UNSUPPORTED, "head size D=%lld not built (16, 32, 64, 128)", (long long)D);
   if (B > kI32Max || H > kI32Max || Nq > kI32Max || Nk > kI32Max || B * H > kI32Max ||
@@ -254,7 +252,7 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
                                 "B*Hkv*Nk < 2^31)");
   if (B == 0 || H == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
 
-  const int64_t elem = 2;
+  const int64_t elem = dtype == ATTN_F32 ? 4 : 2;
   const int64_t qbytes = B * H * Nq * D * elem;
   const int64_t kbytes = B * Hkv * Nk * D * elem;
   const int64_t sbytes = B * H * Nq * 4;
@@ -314,7 +312,8 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
     e = hipMallocAsync(&scratch, sb, p.stream);
     if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of backward scratch");
   }
-  e = attn::launch_bwd_mfma(p, static_cast<float*>(scratch));
+  e = dtype == ATTN_F32 ? attn::launch_bwd_f32(p, static_cast<float*>(scratch))
+                        : attn::launch_bwd_mfma(p, static_cast<float*>(scratch));
   const hipError_t ef = scratch ? hipFreeAsync(scratch, p.stream) : hipSuccess;
   if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of backward scratch");

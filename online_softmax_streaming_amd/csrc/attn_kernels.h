@@ -101,6 +101,9 @@ struct BwdProblem {
 };
 size_t bwd_scratch_bytes(const BwdProblem& p);
 hipError_t launch_bwd_mfma(const BwdProblem& p, float* scratch);
+// FP32 inputs: the same two-kernel backward on the vector ALUs (bwd_f32.hip),
+// same scratch layout.
+hipError_t launch_bwd_f32(const BwdProblem& p, float* scratch);
 
 // Row count above which attn_fwd takes the prefill kernels.
 constexpr int64_t kDecodeMaxNq = 8;

@@ -240,7 +240,8 @@ def _bwd(attn, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=0), 2),                       # FP32 backward is not built
+    (dict(dtype=0, d=48), 2),                 # FP32: D not built
+    (dict(dtype=0, dq=(1 << 24) + 24576), 1),  # FP32 (4-byte elements): dQ overlaps Q
     (dict(dtype=7), 1),
     (dict(causal=2), 1),
     (dict(hkv=3), 1),

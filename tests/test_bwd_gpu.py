@@ -1,4 +1,5 @@
-"""GPU parity of the attention backward (attn_bwd) against the FP64 oracle.
+"""GPU parity of the attention backward (attn_bwd) against the FP64 oracle,
+for bf16, f16 and FP32 inputs.
 
 Each case runs the forward (attn_fwd_gqa with row states) and then attn_bwd
 through the C ABI, and compares dQ, dK, dV element by element with
@@ -23,6 +24,22 @@ of a group for grouped K/V.  The check is
 where u |ref| is the output cast, the factor 2 covers the FP32 rounding the
 derivation leaves out (2^-24 per term), and a is 2^-25 for f16 or 1e-37
 for bf16.
+
+FP32 inputs (vector-ALU kernels, nothing rounded to a narrower type): with
+g = 2^-24, every sum of n FP32 products is off by at most about n g times
+the sum of the products' magnitudes.  So the score s is off by
+e_s = (D + 2) g scale (|Q| |K|^T); the forward's l (a sum of Nk weights) by a
+relative (Nk + 8) g, and forming exp(s - lse) adds a few ulps of its
+argument, so P is off by a relative
+    eps_P = e_s + (Nk + 8) g + 8 g (|lse| + |s|) + 4 g.
+The forward's O is off by eps_O (P |V|) with eps_O = 2 max(eps_P) + (Nk + 8) g,
+so Delta is off by |dO| . eps_O (P |V|) + (D + 2) g (|dO| . |O|); dP by
+(D + 2) g (|dO| |V|^T).  Then
+    E = eps_P P |dP - Delta| + P (e_dP + e_Delta) + g P |dP - Delta|
+bounds the dS error, and b_dQ = scale (E |K| + (Nk + 2) g |dS| |K|),
+b_dK = scale (E^T |Q| + (Nq + 2) g |dS|^T |Q|),
+b_dV = (eps_P P)^T |dO| + (Nq + 2) g P^T |dO|, checked as
+|got - ref| <= 2 b + g |ref| + 1e-30.
 """
 
 import numpy as np
@@ -34,9 +51,9 @@ from online_softmax_streaming_amd.workloads import WORKLOADS, make_qkv, random_d
 
 pytestmark = pytest.mark.gpu
 
-U = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+U = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -24}
 SUB = {"bf16": 2.0 ** -134, "f16": 2.0 ** -25}
-A = {"bf16": 1e-37, "f16": 2.0 ** -25}
+A = {"bf16": 1e-37, "f16": 2.0 ** -25, "f32": 1e-30}
 
 
 @pytest.fixture(scope="module")
@@ -74,10 +91,43 @@ def _head_bounds(q, k, v, do, causal, scale, dtype):
             (2 * u * p + sub * vis).T @ np.abs(do))
 
 
+def _head_bounds_f32(q, k, v, do, causal, scale):
+    """Error bounds (dQ, dK, dV) of one head for FP32 inputs; see the module
+    docstring."""
+    g = 2.0 ** -24
+    nq, d = q.shape
+    nk = k.shape[0]
+    p = oracle.probabilities(q, k, causal, scale)
+    s = scale * (q @ k.T)
+    vis = p > 0
+    lse = np.zeros(nq)
+    for i in range(nq):
+        if vis[i].any():
+            mx = s[i][vis[i]].max()
+            lse[i] = mx + np.log(np.exp(s[i][vis[i]] - mx).sum())
+    e_s = (d + 2) * g * scale * (np.abs(q) @ np.abs(k).T)
+    eps_p = e_s + (nk + 8) * g + 8 * g * (np.abs(lse)[:, None] + np.abs(s)) + 4 * g
+    eps_p = np.where(vis, eps_p, 0.0)
+    o = p @ v
+    eps_o = 2 * eps_p.max(axis=1) + (nk + 8) * g
+    e_o = eps_o[:, None] * (p @ np.abs(v))
+    dp = do @ v.T
+    delta = (do * o).sum(axis=1)
+    e_delta = (np.abs(do) * e_o).sum(axis=1) + (d + 2) * g * (np.abs(do) * np.abs(o)).sum(axis=1)
+    e_dp = (d + 2) * g * (np.abs(do) @ np.abs(v).T)
+    gap = np.abs(dp - delta[:, None])
+    ds = p * (dp - delta[:, None])
+    e_ds = eps_p * p * gap + p * (e_dp + e_delta[:, None]) + g * p * gap
+    b_dq = scale * (e_ds @ np.abs(k) + (nk + 2) * g * (np.abs(ds) @ np.abs(k)))
+    b_dk = scale * (e_ds.T @ np.abs(q) + (nq + 2) * g * (np.abs(ds).T @ np.abs(q)))
+    b_dv = (eps_p * p).T @ np.abs(do) + (nq + 2) * g * (p.T @ np.abs(do))
+    return b_dq, b_dk, b_dv
+
+
 def _check(lib, q, k, v, do, causal, got, heads=None):
     """Compare got = (dq, dk, dv) with the oracle; ``heads`` limits the
     check to some (b, kv-head) pairs (all when None)."""
-    dtype = {torch.bfloat16: "bf16", torch.float16: "f16"}[q.dtype]
+    dtype = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[q.dtype]
     d = q.shape[-1]
     scale = lib.default_scale(d)
     g = q.shape[1] // k.shape[1]
@@ -93,7 +143,8 @@ def _check(lib, q, k, v, do, causal, got, heads=None):
         for h in range(hk * g, hk * g + g):
             args = (qd[b, h], kd[b, hk], vd[b, hk], dod[b, h], causal, scale)
             wq, wk, wv = oracle.attention_backward_head(*args)
-            mq, mk, mv = _head_bounds(*args, dtype)
+            mq, mk, mv = (_head_bounds_f32(*args) if dtype == "f32"
+                          else _head_bounds(*args, dtype))
             want_dk += wk
             want_dv += wv
             bnd_dk += mk
@@ -116,7 +167,7 @@ def _assert_close(got, want, b, dtype, what):
                           f"{np.abs(got - want).max():.3g}, max |ref| {np.abs(want).max():.3g}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("b,h,nq,nk,d", [
     (1, 2, 200, 200, 128),
@@ -135,16 +186,17 @@ def test_parity(lib, dtype, causal, b, h, nq, nk, d):
     _check(lib, q, k, v, do, causal, got)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("h,hkv,nq,nk,d", [(8, 2, 259, 517, 128), (4, 1, 300, 300, 64),
                                            (6, 3, 130, 70, 32)])
-def test_grouped_kv(lib, causal, h, hkv, nq, nk, d):
-    q, k, v, do = _inputs(2, h, hkv, nq, nk, d, "bf16", seed=h + hkv + nq)
+def test_grouped_kv(lib, dtype, causal, h, hkv, nq, nk, d):
+    q, k, v, do = _inputs(2, h, hkv, nq, nk, d, dtype, seed=h + hkv + nq)
     got = _run(lib, q, k, v, do, causal)
     _check(lib, q, k, v, do, causal, got)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_large_logits_and_rising_keys(lib, dtype):
     # Scores spread over tens of units and a key ramp: P spans many orders
     # of magnitude and the lse must come from the forward's exact row max.
@@ -197,16 +249,18 @@ def test_side_stream(lib):
     _check(lib, q, k, v, do, True, got)
 
 
-def test_tolerance_rejects_planted_mistakes(lib):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tolerance_rejects_planted_mistakes(lib, dtype):
     # The bound must be tight enough to catch plausible kernel mistakes.  Each
     # is planted in the oracle on the CPU; the GPU result must then fail the
     # bound against the planted version.
-    q, k, v, do = _inputs(1, 1, 1, 200, 200, 64, "bf16", seed=13)
+    q, k, v, do = _inputs(1, 1, 1, 200, 200, 64, dtype, seed=13)
     got = _run(lib, q, k, v, do, True)
     scale = lib.default_scale(64)
     qd, kd, vd, dod = (t.cpu().double().numpy()[0, 0] for t in (q, k, v, do))
     gq, gk, gv = (t.cpu().double().numpy()[0, 0] for t in got)
-    mq, mk, mv = _head_bounds(qd, kd, vd, dod, True, scale, "bf16")
+    mq, mk, mv = (_head_bounds_f32(qd, kd, vd, dod, True, scale) if dtype == "f32"
+                  else _head_bounds(qd, kd, vd, dod, True, scale, dtype))
     p = oracle.probabilities(qd, kd, True, scale)
     ds_bad = oracle.softmax_vjp(p, dod @ vd.T, bugs=("unweighted_reduction",))
     ds = oracle.softmax_vjp(p, dod @ vd.T)
@@ -217,7 +271,7 @@ def test_tolerance_rejects_planted_mistakes(lib):
         "diagonal masked (dV)": (gv, p_nodiag.T @ dod, mv),
     }
     for name, (g, bad, b) in planted.items():
-        assert np.any(np.abs(g - bad) > _bound(b, bad, "bf16")), name
+        assert np.any(np.abs(g - bad) > _bound(b, bad, dtype)), name
 
 
 @pytest.mark.parametrize("name", ["headline_causal_bf16", "headline_noncausal_bf16"])

@@ -8,9 +8,10 @@
 // instruction faster than its vector FMA path by enough to matter here.
 //
 // One workgroup = 128 threads = 128/TPQ query rows; a row's features are
-// split over TPQ threads (TPQ = 2 for D = 128, so a thread keeps at most 64
-// features of q and 64 of the running output in registers).  Key tiles of
-// 32 rows are staged in LDS and read by broadcast.
+// split over TPQ threads (by default TPQ = 2 for D = 128, so a thread keeps
+// at most 64 features of q and 64 of the running output in registers; see
+// kTpqWide for small problems).  Key tiles of 32 rows are staged in LDS and
+// read by broadcast.
 
 #include "attn_device.h"
 #include "attn_kernels.h"
@@ -52,12 +53,20 @@ enum : int { kModeBatched = 0, kModeVarlen = 1, kModeMasked = 2, kModeDropout = 
 constexpr int kThreads = 128;
 constexpr int kBNF = 32;
 
-template <int D, bool CAUSAL, int MODE>
+// Threads per query row: the default keeps at most 64 features of q and of
+// the running output per thread; the wide split (8 features per thread)
+// serves problems too small to fill the GPU, trading a few lane exchanges
+// per key for a quarter to a sixteenth of the serial work per thread.
+template <int D>
+constexpr int kTpqDefault = D > 64 ? 2 : 1;
+template <int D>
+constexpr int kTpqWide = D / 8;
+
+template <int D, int TPQ, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
   constexpr bool VARLEN = MODE == kModeVarlen;
   constexpr bool MASKED = MODE == kModeMasked;
   constexpr bool DROPOUT = MODE == kModeDropout;
-  constexpr int TPQ = D > 64 ? 2 : 1;
   constexpr int DT = D / TPQ;
   constexpr int QPB = kThreads / TPQ;
   constexpr int BN = kBNF;
@@ -146,7 +155,8 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
       float dot = 0.f;
 #pragma unroll
       for (int d = 0; d < DT; ++d) dot = __builtin_fmaf(q[d], Ks[jj * D + part * DT + d], dot);
-      if (TPQ == 2) dot += __shfl_xor(dot, 1);
+#pragma unroll
+      for (int o = 1; o < TPQ; o <<= 1) dot += __shfl_xor(dot, o);  // the row's TPQ lanes
       const int j = j0 + jj;
       bool vis = j < Nk && (!CAUSAL || j <= qrow + off);
       if (MASKED) vis = vis && (win <= 0 || j > qrow + off - win) && ((mw >> jj) & 1u);
@@ -203,9 +213,8 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
   }
 }
 
-template <int D, bool CAUSAL, int MODE>
+template <int D, int TPQ, bool CAUSAL, int MODE>
 hipError_t launch_typed(const Problem& p) {
-  constexpr int TPQ = D > 64 ? 2 : 1;
   constexpr int QPB = kThreads / TPQ;
   F32Args a;
   a.q = static_cast<const float*>(p.q);
@@ -235,20 +244,34 @@ hipError_t launch_typed(const Problem& p) {
   a.drop_t = p.drop_t;
   a.keep_gain = (float)(65536.0 / (65536.0 - (double)p.drop_t));
   const int64_t grid = p.B * p.H * a.nqt;
-  hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL, MODE>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((prefill_f32_kernel<D, TPQ, CAUSAL, MODE>), dim3((unsigned)grid), dim3(kThreads), 0,
                      p.stream, a);
   return hipGetLastError();
 }
 
+template <int D, int TPQ>
+hipError_t launch_mode(const Problem& p) {
+  if (p.cu_q)
+    return p.causal ? launch_typed<D, TPQ, true, kModeVarlen>(p)
+                    : launch_typed<D, TPQ, false, kModeVarlen>(p);
+  if (p.mask || p.window > 0)
+    return p.causal ? launch_typed<D, TPQ, true, kModeMasked>(p)
+                    : launch_typed<D, TPQ, false, kModeMasked>(p);
+  if (p.dropout)
+    return p.causal ? launch_typed<D, TPQ, true, kModeDropout>(p)
+                    : launch_typed<D, TPQ, false, kModeDropout>(p);
+  return p.causal ? launch_typed<D, TPQ, true, kModeBatched>(p)
+                  : launch_typed<D, TPQ, false, kModeBatched>(p);
+}
+
 template <int D>
 hipError_t launch_d(const Problem& p) {
-  if (p.cu_q)
-    return p.causal ? launch_typed<D, true, kModeVarlen>(p) : launch_typed<D, false, kModeVarlen>(p);
-  if (p.mask || p.window > 0)
-    return p.causal ? launch_typed<D, true, kModeMasked>(p) : launch_typed<D, false, kModeMasked>(p);
-  if (p.dropout)
-    return p.causal ? launch_typed<D, true, kModeDropout>(p) : launch_typed<D, false, kModeDropout>(p);
-  return p.causal ? launch_typed<D, true, kModeBatched>(p) : launch_typed<D, false, kModeBatched>(p);
+  // Fewer default workgroups than half the CUs: the wide split.  The rule
+  // depends only on (B, H, Nq), so every mode of one problem shape splits
+  // its rows the same way and computes each row identically.
+  constexpr int64_t qpb = kThreads / kTpqDefault<D>;
+  if (p.B * p.H * ((p.Nq + qpb - 1) / qpb) < 128) return launch_mode<D, kTpqWide<D>>(p);
+  return launch_mode<D, kTpqDefault<D>>(p);
 }
 
 }  // namespace

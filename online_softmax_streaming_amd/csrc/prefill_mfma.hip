@@ -73,7 +73,7 @@ struct PrefillArgs {
   // [H, total_q].  nqt is then the tile count of the longest sequence.
   const int* cu_q;
   const int* cu_k;
-  int H, Hkv;
+  int B, H, Hkv;
   int total_q, total_k;
   // Masked mode (MASKED kernels only, batched layout): an optional
   // bit-packed mask, bit j % 32 of word j / 32 of row (b, h, i) at
@@ -156,7 +156,11 @@ void prefill_mfma_kernel(PrefillArgs a) {
   if (VARLEN) {
     // Sequence bounds are clamped into the packed tensors, so no value of
     // cu_q / cu_k can address memory outside them.
-    const int b = bh / a.H, h = bh - b * a.H;
+    // Head-major order: each XCD's contiguous range of workgroups then holds
+    // a few heads of every sequence, so ragged sequence lengths do not pile
+    // the long sequences onto some XCDs (batch-major order would give each
+    // XCD a few whole sequences).
+    const int h = bh / a.B, b = bh - h * a.B;
     const int q0 = min(max(a.cu_q[b], 0), a.total_q);
     const int q1 = min(max(a.cu_q[b + 1], q0), a.total_q);
     const int k0 = min(max(a.cu_k[b], 0), a.total_k);
@@ -541,6 +545,7 @@ hipError_t launch_typed(const Problem& p) {
   a.nqt = (int)((p.Nq + BM - 1) / BM);  // varlen: p.Nq is the longest sequence
   a.cu_q = p.cu_q;
   a.cu_k = p.cu_k;
+  a.B = (int)p.B;
   a.H = (int)p.H;
   a.Hkv = (int)p.Hkv;
   a.total_q = (int)p.total_q;

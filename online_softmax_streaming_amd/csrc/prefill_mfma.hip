@@ -131,6 +131,8 @@ void prefill_mfma_kernel(PrefillArgs a) {
   // direct-to-LDS loads into one from the operand reads of the other.
   __shared__ __attribute__((aligned(1024))) unsigned char smem0[2][TILE];  // [K, V]
   __shared__ __attribute__((aligned(1024))) unsigned char smem1[2][TILE];
+  // Per-wave votes on whether a future key tile is needed (masked mode).
+  __shared__ int tile_need[2][NW];
   auto tile_ptr = [&](int buf, int kv) __attribute__((always_inline)) -> unsigned char* {
     return buf == 0 ? &smem0[kv][0] : &smem1[kv][0];
   };
@@ -466,23 +468,68 @@ void prefill_mfma_kernel(PrefillArgs a) {
     };
 
     if (ntiles > t_first) {
-      load_tile(t_first * BN, 0);
-      // Mask words of the next tile, fetched one tile ahead.
-      uint32_t nw0 = mask_word(2 * t_first), nw1 = mask_word(2 * t_first + 1);
-      __syncthreads();
       const int q_last = min(qw0 + 32, Nq) - 1;  // last real row of this wave
+      // Whether the causal rule and the window leave tile u any key this
+      // wave's rows may see.
+      auto wave_active = [&](int u) __attribute__((always_inline)) {
+        const int ju = u * BN;
+        bool act = qw0 < Nq && (!CAUSAL || ju <= q_last + off);
+        if (MASKED && win > 0) act = act && ju + BN - 1 > qw0 + off - win;
+        return act;
+      };
+      // Under a mask, tiles no row of the workgroup may see are neither
+      // staged nor computed: each wave votes on tile t+2 during step t (its
+      // rows' mask words are fetched two tiles ahead), the votes meet in LDS
+      // across the step's barrier, and step t+1 stages tile t+2 only if some
+      // wave needs it.  Flags of tile u live in tile_need[u & 1]; they are
+      // written in step u-2 and read right after that step's barrier, and
+      // the next write to the same slot comes two barriers later.
+      const bool skip_tiles = MASKED && a.mask != nullptr;
+      auto any_need = [&](int slot) __attribute__((always_inline)) {
+        int v = 0;
+  #pragma unroll
+        for (int w = 0; w < NW; ++w) v |= tile_need[slot][w];
+        return __builtin_amdgcn_readfirstlane(v) != 0;
+      };
+      // Mask words of this lane's row: tile t (mw), t+1 (nw), t+2 (xw).
+      uint32_t nw0 = mask_word(2 * t_first), nw1 = mask_word(2 * t_first + 1);
+      uint32_t xw0 = 0, xw1 = 0;
+      bool need_cur = true, need_next = true;
+      if (skip_tiles) {
+        xw0 = mask_word(2 * t_first + 2);
+        xw1 = mask_word(2 * t_first + 3);
+        const bool n0 = wave_active(t_first) && __builtin_amdgcn_ballot_w64((nw0 | nw1) != 0u) != 0;
+        const bool n1 = t_first + 1 < ntiles && wave_active(t_first + 1) &&
+                        __builtin_amdgcn_ballot_w64((xw0 | xw1) != 0u) != 0;
+        if (lane == 0) {
+          tile_need[t_first & 1][wave] = n0;
+          tile_need[(t_first + 1) & 1][wave] = n1;
+        }
+        __syncthreads();
+        need_cur = any_need(t_first & 1);
+        need_next = any_need((t_first + 1) & 1);
+      }
+      if (need_cur) load_tile(t_first * BN, 0);
+      __syncthreads();
       auto step = [&](auto bufc, int t) {
         constexpr int buf = decltype(bufc)::value;
         const int j0 = t * BN;
         const bool more = t + 1 < ntiles;
-        if (more) load_tile(j0 + BN, buf ^ 1);  // in flight while this tile is computed
+        if (more && need_next) load_tile(j0 + BN, buf ^ 1);  // in flight while this tile is computed
         const uint32_t mw0 = nw0, mw1 = nw1;
+        uint32_t fw0 = 0, fw1 = 0;  // words of tile t+2 (tile skipping only)
         if (MASKED && more) {
-          nw0 = mask_word(j0 / 32 + 2);
-          nw1 = mask_word(j0 / 32 + 3);
+          if (skip_tiles) {
+            nw0 = xw0;
+            nw1 = xw1;
+            fw0 = mask_word(j0 / 32 + 4);
+            fw1 = mask_word(j0 / 32 + 5);
+          } else {
+            nw0 = mask_word(j0 / 32 + 2);
+            nw1 = mask_word(j0 / 32 + 3);
+          }
         }
-        bool active = qw0 < Nq && (!CAUSAL || j0 <= q_last + off);
-        if (MASKED && win > 0) active = active && j0 + BN - 1 > qw0 + off - win;
+        bool active = need_cur && wave_active(t);
         // A tile none of this wave's rows may see under the mask is skipped.
         if (MASKED && a.mask) active = active && __builtin_amdgcn_ballot_w64((mw0 | mw1) != 0u) != 0;
         if (active) {
@@ -490,8 +537,19 @@ void prefill_mfma_kernel(PrefillArgs a) {
           if (MASKED) need_mask = need_mask || a.mask || (win > 0 && j0 <= q_last + off - win);
           compute(bufc, j0, need_mask, mw0, mw1);
         }
+        if (skip_tiles) {
+          const bool n2 = t + 2 < ntiles && wave_active(t + 2) &&
+                          __builtin_amdgcn_ballot_w64((fw0 | fw1) != 0u) != 0;
+          if (lane == 0) tile_need[t & 1][wave] = n2;  // slot of tile t+2
+          xw0 = fw0;
+          xw1 = fw1;
+        }
         // Buffer buf^1 was last read in step t-1, before that step's barrier.
         __syncthreads();
+        if (skip_tiles) {
+          need_cur = need_next;
+          need_next = any_need(t & 1);
+        }
       };
       for (int t = t_first; t < ntiles; t += 2) {
         step(std::integral_constant<int, 0>{}, t);

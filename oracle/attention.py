@@ -18,9 +18,11 @@ section "Scope and contracts", streaming_attention row: single-head
 self-attention Q/K/V[N, D], scale 1/sqrt(D) (here an explicit argument),
 diagonal included when causal.  Answer-key page ("Compare reasoning after your
 own attempt"), closing note of "Reference tradeoffs to challenge": the
-attention oracle materialises FP64 scores.  Readings where the pages are
-silent (batched [B, H, N, D] layout, causal alignment for Nq != Nk, rows with
-no visible key, explicit scale) are listed in the design doc.
+attention oracle materialises FP64 scores.  Where the pages are silent this
+module reads them as follows: heads are batched as [B, H, N, D]; with Nq != Nk
+the causal rule aligns the last query with the last key (key j is visible to
+query i iff j <= i + Nk - Nq); a row with no visible key returns zeros with
+row state (m, l) = (-inf, 0); the scale is an explicit argument.
 
 The two-pass form above is the plain definition of softmax(scale Q K^T) V with
 the maximum subtracted for stability ("Kernel Notes & Checklist", section 4,

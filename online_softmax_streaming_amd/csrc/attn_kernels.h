@@ -101,6 +101,10 @@ struct BwdProblem {
 };
 size_t bwd_scratch_bytes(const BwdProblem& p);
 hipError_t launch_bwd_mfma(const BwdProblem& p, float* scratch);
+// Plain batched bf16/f16 prefill with the keys of each 32-row block split
+// over the waves of a workgroup and merged in LDS (prefill_splitk.hip), for
+// problems too small to fill the GPU.
+hipError_t launch_prefill_splitk(const Problem& p);
 // FP32 inputs: the same two-kernel backward on the vector ALUs (bwd_f32.hip),
 // same scratch layout.
 hipError_t launch_bwd_f32(const BwdProblem& p, float* scratch);

@@ -647,14 +647,11 @@ hipError_t launch_d(const Problem& p) {
     return p.causal ? launch_typed<T, D, kWaves, true, kModeDropout>(p)
                     : launch_typed<T, D, kWaves, false, kModeDropout>(p);
   // A small problem (fewer workgroups of kWaves waves than half the CUs)
-  // runs in two-wave workgroups: each wave's rows still stream every key, but
-  // four times as many workgroups spread over the CUs and each wave gets its
-  // SIMD alone, so the longest row block finishes sooner.
+  // splits the keys of each 32-row block over the waves of a workgroup
+  // (prefill_splitk.hip): more waves busy, each with a shorter chain.
   const int64_t nqt = (p.Nq + 32 * kWaves - 1) / (32 * kWaves);
   const int64_t wgs = p.B * p.H * (p.causal ? (nqt + 1) / 2 : nqt);
-  if (wgs < kSmallGridWgs)
-    return p.causal ? launch_typed<T, D, 2, true, kModeBatched>(p)
-                    : launch_typed<T, D, 2, false, kModeBatched>(p);
+  if (wgs < kSmallGridWgs) return launch_prefill_splitk(p);
   return p.causal ? launch_typed<T, D, kWaves, true, kModeBatched>(p)
                   : launch_typed<T, D, kWaves, false, kModeBatched>(p);
 }

@@ -357,23 +357,27 @@ def test_online_merge_batch_matches_oracle():
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("nq,nk,d", [(259, 259, 128), (130, 333, 64), (333, 130, 64),
-                                     (64, 64, 32), (700, 700, 16)])
-def test_small_grid_variant_matches_wide_grid(dtype, causal, nq, nk, d):
-    # A problem with few workgroups runs in two-wave workgroups, a large one
-    # in eight-wave workgroups.  Each row's arithmetic is the same in both
-    # (same key tiles in the same order), so the heads of a small problem,
-    # repeated 64 times to make a large one, must come out bit for bit equal.
+                                     (64, 64, 32), (700, 700, 16), (40, 2000, 64),
+                                     (100, 1000, 128)])
+def test_small_grid_split_and_wide_grid(dtype, causal, nq, nk, d):
+    # A problem with few workgroups splits the keys of each 32-row block over
+    # the waves of a workgroup and merges their states; a large one streams
+    # them in one wave.  Both are checked against the oracle: the small
+    # problem in full, the same heads repeated 64 times on three repeats.
     _say(f"grid variants dtype={dtype} causal={causal} Nq={nq} Nk={nk} D={d}")
     q, k, v = random_qkv(1, 2, nq, nk, d, dtype, seed=nq + 7 * nk + d, device=DEV, k_ramp=0.01)
-    small, sm, sl = attn_fwd_stats(q, k, v, causal=causal)
+    scale = default_scale(d)
+    small, sm, sl = attn_fwd_stats(q, k, v, causal=causal, scale=scale)
     wide, wm, wl = attn_fwd_stats(q.repeat(64, 1, 1, 1), k.repeat(64, 1, 1, 1),
-                                  v.repeat(64, 1, 1, 1), causal=causal)
+                                  v.repeat(64, 1, 1, 1), causal=causal, scale=scale)
+    again = attn_fwd(q, k, v, causal=causal, scale=scale)
     torch.cuda.synchronize()
-    for rep in (0, 37, 63):
-        assert torch.equal(wide[rep], small[0]), f"output differs in repeat {rep}"
-        assert torch.equal(wm[rep], sm[0]) and torch.equal(wl[rep], sl[0])
-    err = _compare_full(q, k, v, causal, default_scale(d), small, TOL[dtype], sm, sl)
+    assert torch.equal(again, small), "the split path is not deterministic"
+    err = _compare_full(q, k, v, causal, scale, small, TOL[dtype], sm, sl)
     _record(f"small grid {dtype} causal={causal} D={d} Nq={nq} Nk={nk}", err, TOL[dtype])
+    for rep in (0, 37, 63):
+        _compare_full(q, k, v, causal, scale, wide[rep:rep + 1], TOL[dtype], wm[rep:rep + 1],
+                      wl[rep:rep + 1])
 
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -80,8 +80,9 @@ extern "C" {
  *                 Q, K or V.  K and V may be NULL when Nk == 0.
  *   B, H, Nq, Nk  >= 0.  B, H or Nq == 0 is a no-op returning ATTN_OK.
  *                 Nk == 0 writes out = 0.  Per head, Nq*D and Nk*D must be
- *                 < 2^31, and B*H < 2^31; element offsets across heads are
- *                 64-bit, so whole tensors may exceed 2^31 elements.
+ *                 < 2^31, and B*H and B*H*Nq (rows) < 2^31; element offsets
+ *                 across heads are 64-bit, so whole tensors may exceed 2^31
+ *                 elements.
  *   D             head size: 16, 32, 64 or 128 (else ATTN_E_UNSUPPORTED).
  *   causal        0 or 1.
  *   scale         logit scale, finite and > 0 (the pages use 1/sqrt(D)).

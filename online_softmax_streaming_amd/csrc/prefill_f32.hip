@@ -13,6 +13,8 @@
 // kTpqWide for small problems).  Key tiles of 32 rows are staged in LDS and
 // read by broadcast.
 
+#include <climits>
+
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -61,9 +63,17 @@ template <int D>
 constexpr int kTpqDefault = D > 64 ? 2 : 1;
 template <int D>
 constexpr int kTpqWide = D / 8;
+// Key-split groups of the wide split (two for D = 128, whose four-group
+// workgroup would need more than 256 registers per thread in dropout mode).
+template <int D>
+constexpr int kKsfWide = D > 64 ? 2 : 4;
 
-template <int D, int TPQ, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
+// KSF groups of kThreads threads split the key tiles of the workgroup's rows
+// (group g takes tiles t_first + g, t_first + g + KSF, ...) and merge their
+// states at the end (answer-key row A1); KSF = 1 streams every tile in one
+// group.
+template <int D, int TPQ, bool CAUSAL, int MODE, int KSF>
+__global__ __launch_bounds__(kThreads * KSF) void prefill_f32_kernel(F32Args a) {
   constexpr bool VARLEN = MODE == kModeVarlen;
   constexpr bool MASKED = MODE == kModeMasked;
   constexpr bool DROPOUT = MODE == kModeDropout;
@@ -71,8 +81,8 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
   constexpr int QPB = kThreads / TPQ;
   constexpr int BN = kBNF;
 
-  __shared__ __attribute__((aligned(16))) float Ks[BN * D];
-  __shared__ __attribute__((aligned(16))) float Vs[BN * D];
+  __shared__ __attribute__((aligned(16))) float Ksm[KSF][BN * D];
+  __shared__ __attribute__((aligned(16))) float Vsm[KSF][BN * D];
 
   const int bh = blockIdx.x / a.nqt;
   const int qt = blockIdx.x - bh * a.nqt;
@@ -104,7 +114,10 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
   const float* __restrict__ Vh = a.v + kbase;
   float* __restrict__ Oh = a.o + qbase;
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x % kThreads;
+  const int grp = threadIdx.x / kThreads;
+  float* __restrict__ Ks = Ksm[grp];
+  float* __restrict__ Vs = Vsm[grp];
   const int part = tid % TPQ;
   const int i0 = qt * QPB;
   const int qrow = i0 + tid / TPQ;
@@ -129,10 +142,13 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
     mrow = a.mask + (int64_t)b * a.mask_sb + (int64_t)h * a.mask_sh + (int64_t)qrow * a.mask_words;
   }
 
-  for (int t = t_first; t < ntiles; ++t) {
+  for (int t0 = t_first; t0 < ntiles; t0 += KSF) {
+    const int t = t0 + grp;
+    const bool live = KSF == 1 || t < ntiles;  // this group has a tile in this round
     const int j0 = t * BN;
     // Stage the tile: 16-byte loads, rows past Nk zero.
-    for (int e = tid; e < BN * D / 4; e += kThreads) {
+#pragma unroll 4
+    for (int e = tid; live && e < BN * D / 4; e += kThreads) {
       const int row = e / (D / 4), col = e - row * (D / 4);
       const int j = j0 + row;
       f32x4 kv = f32x4{}, vv = f32x4{};
@@ -144,8 +160,14 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
       *reinterpret_cast<f32x4*>(&Vs[row * D + col * 4]) = vv;
     }
     __syncthreads();
+    if (!live) {
+      __syncthreads();
+      continue;
+    }
 
-    // The row's mask bits for keys j0 .. j0+31 (all set without a mask).
+    // The row's mask bits for keys j0 .. j0+31 (all set without a mask) and
+    // the window's lower limit (visible iff j > wlo), one compare per key.
+    const int wlo = win > 0 ? qrow + off - win : INT_MIN;
     uint32_t mw = ~0u;
     if (MASKED && a.mask) mw = mrow && j0 / 32 < a.mask_words ? mrow[j0 / 32] : 0u;
     float s[BN];
@@ -159,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
       for (int o = 1; o < TPQ; o <<= 1) dot += __shfl_xor(dot, o);  // the row's TPQ lanes
       const int j = j0 + jj;
       bool vis = j < Nk && (!CAUSAL || j <= qrow + off);
-      if (MASKED) vis = vis && (win <= 0 || j > qrow + off - win) && ((mw >> jj) & 1u);
+      if (MASKED) vis = vis && j > wlo && ((mw >> jj) & 1u);
       // Rounded product kept apart from the later subtraction, so the
       // largest score gives exactly 2^0 = 1.
       s[jj] = vis ? dot * c : kNegInf;
@@ -200,6 +222,36 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
     __syncthreads();
   }
 
+  if constexpr (KSF > 1) {
+    // Merge (answer-key row A1): groups 1..KSF-1 leave (m, l, acc) in LDS;
+    // group 0 rescales each state to the common reference and sums.
+    __shared__ float mst[KSF - 1][DT + 2][kThreads];
+    if (grp > 0) {
+      mst[grp - 1][0][tid] = m_run;
+      mst[grp - 1][1][tid] = l_run;
+  #pragma unroll
+      for (int d = 0; d < DT; ++d) mst[grp - 1][2 + d][tid] = acc[d];
+    }
+    __syncthreads();
+    if (grp > 0) return;
+    float M = m_run;
+  #pragma unroll
+    for (int g = 1; g < KSF; ++g) M = fmaxf(M, mst[g - 1][0][tid]);
+    const float ref = pinned_ref(M);
+    const float w0 = exp2_hw(m_run - ref);
+    l_run *= w0;
+  #pragma unroll
+    for (int d = 0; d < DT; ++d) acc[d] *= w0;
+  #pragma unroll
+    for (int g = 1; g < KSF; ++g) {
+      const float wg = exp2_hw(mst[g - 1][0][tid] - ref);
+      l_run = __builtin_fmaf(mst[g - 1][1][tid], wg, l_run);
+  #pragma unroll
+      for (int d = 0; d < DT; ++d) acc[d] = __builtin_fmaf(mst[g - 1][2 + d][tid], wg, acc[d]);
+    }
+    m_run = M;
+  }
+
   if (qrow < Nq) {
     float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     if (DROPOUT) inv *= a.keep_gain;
@@ -213,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(F32Args a) {
   }
 }
 
-template <int D, int TPQ, bool CAUSAL, int MODE>
+template <int D, int TPQ, bool CAUSAL, int MODE, int KSF>
 hipError_t launch_typed(const Problem& p) {
   constexpr int QPB = kThreads / TPQ;
   F32Args a;
@@ -244,34 +296,35 @@ hipError_t launch_typed(const Problem& p) {
   a.drop_t = p.drop_t;
   a.keep_gain = (float)(65536.0 / (65536.0 - (double)p.drop_t));
   const int64_t grid = p.B * p.H * a.nqt;
-  hipLaunchKernelGGL((prefill_f32_kernel<D, TPQ, CAUSAL, MODE>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((prefill_f32_kernel<D, TPQ, CAUSAL, MODE, KSF>), dim3((unsigned)grid), dim3(kThreads * KSF), 0,
                      p.stream, a);
   return hipGetLastError();
 }
 
-template <int D, int TPQ>
+template <int D, int TPQ, int KSF>
 hipError_t launch_mode(const Problem& p) {
   if (p.cu_q)
-    return p.causal ? launch_typed<D, TPQ, true, kModeVarlen>(p)
-                    : launch_typed<D, TPQ, false, kModeVarlen>(p);
+    return p.causal ? launch_typed<D, TPQ, true, kModeVarlen, KSF>(p)
+                    : launch_typed<D, TPQ, false, kModeVarlen, KSF>(p);
   if (p.mask || p.window > 0)
-    return p.causal ? launch_typed<D, TPQ, true, kModeMasked>(p)
-                    : launch_typed<D, TPQ, false, kModeMasked>(p);
+    return p.causal ? launch_typed<D, TPQ, true, kModeMasked, KSF>(p)
+                    : launch_typed<D, TPQ, false, kModeMasked, KSF>(p);
   if (p.dropout)
-    return p.causal ? launch_typed<D, TPQ, true, kModeDropout>(p)
-                    : launch_typed<D, TPQ, false, kModeDropout>(p);
-  return p.causal ? launch_typed<D, TPQ, true, kModeBatched>(p)
-                  : launch_typed<D, TPQ, false, kModeBatched>(p);
+    return p.causal ? launch_typed<D, TPQ, true, kModeDropout, KSF>(p)
+                    : launch_typed<D, TPQ, false, kModeDropout, KSF>(p);
+  return p.causal ? launch_typed<D, TPQ, true, kModeBatched, KSF>(p)
+                  : launch_typed<D, TPQ, false, kModeBatched, KSF>(p);
 }
 
 template <int D>
 hipError_t launch_d(const Problem& p) {
-  // Fewer default workgroups than half the CUs: the wide split.  The rule
+  // Fewer default workgroups than half the CUs: the wide split, with the
+  // key tiles shared out over kKsfWide thread groups.  The rule
   // depends only on (B, H, Nq), so every mode of one problem shape splits
   // its rows the same way and computes each row identically.
   constexpr int64_t qpb = kThreads / kTpqDefault<D>;
-  if (p.B * p.H * ((p.Nq + qpb - 1) / qpb) < 128) return launch_mode<D, kTpqWide<D>>(p);
-  return launch_mode<D, kTpqDefault<D>>(p);
+  if (p.B * p.H * ((p.Nq + qpb - 1) / qpb) < 128) return launch_mode<D, kTpqWide<D>, kKsfWide<D>>(p);
+  return launch_mode<D, kTpqDefault<D>, 1>(p);
 }
 
 }  // namespace

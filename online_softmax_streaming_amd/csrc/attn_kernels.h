@@ -60,9 +60,13 @@ struct DecodePlan {
   int splits;           // key splits per query row
   int keys_per_split;   // keys each split streams
   size_t scratch_bytes; // partial (m, l, a[D]) states, FP32
+  bool gqa_mfma = false;  // partial states from the grouped-head matrix-core kernel
 };
 DecodePlan plan_decode(const Problem& p);
 hipError_t launch_decode(const Problem& p, const DecodePlan& plan, float* scratch);
+// Partial states of the split-key decode for grouped K/V heads on the matrix
+// cores (decode_gqa.hip); plan from plan_decode.
+hipError_t launch_decode_gqa_partial(const Problem& p, const DecodePlan& plan, float* scratch);
 
 // Nk == 0: out = 0, (m, l) = (-inf, 0) (misc.hip).
 hipError_t launch_fill_empty(const Problem& p);

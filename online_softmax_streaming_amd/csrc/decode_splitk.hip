@@ -264,9 +264,14 @@ hipError_t launch_typed(const Problem& p, const DecodePlan& plan, float* scratch
   while ((int64_t(1) << a.page_shift) < p.page_size) ++a.page_shift;
   a.num_pages = p.num_pages;
   const int64_t rows = p.B * p.H * p.Nq;
-  hipLaunchKernelGGL((decode_partial_kernel<T, D, CAUSAL, PAGED>), dim3((unsigned)rows, plan.splits),
-                     dim3(kThreads), 0, p.stream, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (plan.gqa_mfma) {
+    e = launch_decode_gqa_partial(p, plan, scratch);  // decode_gqa.hip
+  } else {
+    hipLaunchKernelGGL((decode_partial_kernel<T, D, CAUSAL, PAGED>), dim3((unsigned)rows, plan.splits),
+                       dim3(kThreads), 0, p.stream, a);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)rows), dim3(128), 0, p.stream, a);
   return hipGetLastError();
@@ -294,7 +299,38 @@ hipError_t launch_t(const Problem& p, const DecodePlan& plan, float* scratch) {
 
 }  // namespace
 
+// Grouped K/V heads, contiguous K/V, no window, bf16/f16, and the G * Nq
+// rows of a K/V head fit one matrix tile: the partial states come from the
+// matrix-core kernel of decode_gqa.hip, which reads each K/V tile once per
+// group.  Its workgroups are (b, K/V head, split): aim for >= 1024 of them
+// with >= 2 tiles per wave in each split.
+DecodePlan plan_decode_gqa(const Problem& p) {
+  const int64_t kv_rows = p.B * p.Hkv;
+  const int64_t waves = p.D > 64 ? 2 : 4;
+  const int64_t want = (1024 + kv_rows - 1) / kv_rows;
+  int64_t kps = (p.Nk + want - 1) / want;
+  const int64_t min_kps = 64 * waves * 2;
+  if (kps < min_kps) kps = min_kps;
+  kps = (kps + 63) / 64 * 64;
+  int64_t splits = (p.Nk + kps - 1) / kps;
+  if (splits < 1) splits = 1;
+  if (splits > 65535) {
+    splits = 65535;
+    kps = ((p.Nk + splits - 1) / splits + 63) / 64 * 64;
+    splits = (p.Nk + kps - 1) / kps;
+  }
+  DecodePlan plan;
+  plan.splits = (int)splits;
+  plan.keys_per_split = (int)kps;
+  plan.scratch_bytes = (size_t)(p.B * p.H * p.Nq) * (size_t)splits * (size_t)(p.D + 2) * sizeof(float);
+  plan.gqa_mfma = true;
+  return plan;
+}
+
 DecodePlan plan_decode(const Problem& p) {
+  if (!p.table && p.window == 0 && (p.dtype == DType::BF16 || p.dtype == DType::F16) &&
+      p.Hkv > 0 && p.H / p.Hkv > 1 && (p.H / p.Hkv) * p.Nq <= 32)
+    return plan_decode_gqa(p);
   // Aim for >= 4096 workgroups (16 per CU) so the HBM stream is deep enough,
   // but give each split at least 256 keys so the merge stays cheap.  The
   // splits cover the longest visible key range a row can have.

@@ -38,6 +38,12 @@ def _grouped(b, h, hkv, nq, nk, d, dtype, seed):
 @pytest.mark.parametrize("h,hkv,nq,nk,d", [
     (8, 1, 300, 300, 64), (8, 2, 259, 517, 128), (8, 4, 517, 259, 64), (6, 3, 1, 1000, 128),
     (8, 2, 5, 700, 64), (4, 4, 129, 129, 32),
+    # decode with grouped heads: G * Nq rows of a K/V head share one matrix
+    # tile (up to 32), several key splits, ragged and causal key ends
+    (32, 8, 4, 5000, 128), (16, 1, 2, 3001, 64), (32, 1, 1, 2049, 32), (8, 2, 3, 4099, 16),
+    (12, 3, 8, 777, 128),
+    # more than 32 rows per K/V head: the per-row split path
+    (8, 1, 5, 1500, 64),
 ])
 def test_parity(lib, dtype, causal, h, hkv, nq, nk, d):
     q, k, v = _grouped(2, h, hkv, nq, nk, d, dtype, seed=h * 10 + hkv + nq)
@@ -68,7 +74,13 @@ def test_equals_mha_on_repeated_kv(lib, dtype, nq):
     vr = v.repeat_interleave(4, dim=1).contiguous()
     want = lib.attn_fwd(q, kr, vr, causal=True)
     torch.cuda.synchronize()
-    assert torch.equal(got, want)
+    if nq == 1 and dtype != "f32":
+        # A grouped decode packs the group's rows into one matrix tile (each
+        # K/V tile read once); the repeated-head call streams rows one by
+        # one.  Both are checked against the oracle in test_parity.
+        assert float((got.float() - want.float()).abs().max()) <= TOL[dtype]
+    else:
+        assert torch.equal(got, want)
 
 
 def test_hkv_equal_h_is_attn_fwd_stats(lib):

@@ -1,6 +1,6 @@
-// Split-key decode with grouped K/V heads on the matrix cores (bf16 / f16,
-// contiguous K/V): the partial-state kernel of the decode path for
-// G = H / Hkv > 1.
+// Split-key decode with grouped K/V heads on the matrix cores (bf16 / f16):
+// the partial-state kernel of the decode path for G = H / Hkv > 1, over
+// contiguous K/V or a paged cache, with an optional sliding window.
 //
 // With grouped heads the G query heads of a K/V head read the same keys.
 // Streaming them row by row (the vector-ALU partial kernel in
@@ -16,7 +16,22 @@
 // query row to the scratch array the decode path's combine kernel folds
 // (same layout: [row][S][D + 2], m in base-2 units relative to the exact
 // maximum of the split).
+//
+// Paged cache [num_pages, Hkv, page_size, D]: each 16-byte load instruction
+// of a tile moves 512 / D consecutive rows, and with page_size >= 512 / D
+// (both powers of two) those rows sit in one page.  Each instruction then
+// gets a buffer descriptor of its own over that page's rows of this K/V
+// head, so all per-lane offsets stay 32-bit however large the cache is;
+// rows past the sequence's length are outside the descriptor's range and
+// arrive as zeros, and a table entry outside [0, num_pages) gives an empty
+// range and marks its keys absent (masked like keys past the end).  The
+// table is read only for keys below the sequence's length.
+//
+// Sliding window (causal): row i sees keys j with i + off - window < j <=
+// i + off.  The splits cover keys from the lowest such bound over the
+// group's rows, rounded down to a tile boundary.
 
+#include <cstdint>
 #include <type_traits>
 
 #include "attn_kernels.h"
@@ -34,6 +49,14 @@ struct GqaArgs {
   int S;        // splits per row
   int kps;      // keys per split (a multiple of 64)
   float c;      // scale * log2(e)
+  int window;   // 0: none
+  // Paged cache (PAGED kernels only): sequence b's key j is row j % page_size
+  // of page table[b * max_pages + j / page_size]; lens[b] keys.
+  const int* table;
+  const int* lens;
+  int max_pages;
+  int page_shift;  // log2(page_size)
+  int num_pages;
 };
 
 constexpr int kBN = 64;
@@ -44,7 +67,7 @@ constexpr float kRefreshGap = 8.0f;  // base-2 units, as in prefill_mfma.hip
 template <int D>
 constexpr int kWaves = D > 64 ? 2 : 4;  // per-wave double-buffered tiles fit in LDS
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
   typedef typename Mfma<T>::vec8 vec8;
   typedef typename Mfma<T>::vec2 vec2;
@@ -59,6 +82,7 @@ __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
   constexpr int NREG = 16 * NB;
   static_assert(G_::steps_keep_swizzle(), "tile steps must keep the LDS swizzle");
   static_assert(NSLOT % 64 == 0, "a wave moves whole 1 KB LDS blocks");
+  constexpr int RPU = 64 / G_::CPR;  // rows moved by one load instruction
 
   __shared__ __attribute__((aligned(1024))) unsigned char buf0[KS][2][TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char buf1[KS][2][TILE];
@@ -74,7 +98,13 @@ __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
   const int split = blockIdx.y;
   const int bk = blockIdx.x;  // b * Hkv + K/V head
   const int b = bk / a.Hkv, hk = bk - b * a.Hkv;
-  const int Nq = a.Nq, Nk = a.Nk;
+  const int Nq = a.Nq;
+  int Nk = a.Nk;
+  const int* trow = nullptr;
+  if (PAGED) {
+    trow = a.table + (int64_t)b * a.max_pages;
+    Nk = min(max(a.lens[b], 0), a.max_pages << a.page_shift);
+  }
   const int off = Nk - Nq;
   const int h32 = lane >> 5;
   const int l32 = lane & 31;
@@ -84,8 +114,8 @@ __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
   const int g = real ? l32 / Nq : 0;
   const int qi = real ? l32 - g * Nq : 0;
   const int64_t qrow = ((int64_t)b * a.H + (int64_t)hk * a.G + g) * Nq + qi;  // row of [B, H, Nq]
-  const T* Kh = static_cast<const T*>(a.k) + (int64_t)bk * Nk * D;
-  const T* Vh = static_cast<const T*>(a.v) + (int64_t)bk * Nk * D;
+  const T* Kh = static_cast<const T*>(a.k) + (PAGED ? 0 : (int64_t)bk * Nk * D);
+  const T* Vh = static_cast<const T*>(a.v) + (PAGED ? 0 : (int64_t)bk * Nk * D);
   const float c = a.c;
 
   vec8 qf[KC];
@@ -95,7 +125,11 @@ __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
                   : vec8{};
   }
 
-  const int k0 = split * a.kps;
+  // Keys below every row's window are skipped: the splits start at the
+  // lowest visible key of the group (row 0's bound), on a tile boundary.
+  const int win = a.window;
+  const int kbeg = win > 0 ? max(0, off - win + 1) & ~(BN - 1) : 0;
+  const int k0 = kbeg + split * a.kps;
   const int k1 = min(Nk, k0 + a.kps);
   const int t0 = k0 / BN;
   const int t1 = k1 > k0 ? (k1 + BN - 1) / BN : t0;  // tiles [t0, t1) of this split
@@ -130,8 +164,59 @@ __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
 
-  auto load_tile = [&](int t, auto bufc) __attribute__((always_inline)) {
+  // Paged: lane u holds the physical page of the rows that load instruction
+  // u of a tile moves (-1 past the sequence's length), fetched a step before
+  // the tile's loads need it.
+  constexpr int NU = NSLOT / 64;  // load instructions per tile and K or V
+  const int pshift = a.page_shift;
+  auto fetch_pages = [&](int t) __attribute__((always_inline)) -> int {
+    if (!PAGED || t >= t1) return -1;
+    const int j = t * BN + lane * RPU;
+    return lane < NU && j < Nk ? trow[j >> pshift] : -1;
+  };
+  // Per tile buffer, the rows whose page is absent (bit r = row r of the
+  // tile); rows past the sequence's length are handled by the length.
+  uint64_t absent0 = 0, absent1 = 0;
+  auto load_tile = [&](int t, auto bufc, int pv) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
+    if (PAGED) {
+      // Lane u works out instruction u's rows (one page: page_size >= RPU),
+      // its byte offset in the cache and how many of its rows exist; each
+      // instruction then reads them back as scalars for its descriptor.
+      const int ju = t * BN + lane * RPU;
+      const bool inside = lane < NU && ju < Nk;
+      const bool ok = inside && pv >= 0 && pv < a.num_pages;
+      const uint32_t bytes_u = ok ? (uint32_t)min(Nk - ju, RPU) * kpitch : 0u;
+      const uint64_t off_u =
+          ok ? (uint64_t)(((((int64_t)pv * a.Hkv + hk) << pshift) + (ju & ((1 << pshift) - 1))) * D) * 2u
+             : 0u;
+      const uint64_t absent_u = __builtin_amdgcn_ballot_w64(inside && !ok);
+      uint64_t absent = 0;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)off_u, u);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(off_u >> 32), u);
+        const uint32_t bytes = __builtin_amdgcn_readlane(bytes_u, u);
+        const uint64_t off = ((uint64_t)hi << 32) | lo;
+        if ((absent_u >> u) & 1ull) absent |= ((1ull << RPU) - 1) << (u * RPU);
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<unsigned char*>(reinterpret_cast<const unsigned char*>(Kh) + off), 0, (int)bytes,
+            0x00020000);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<unsigned char*>(reinterpret_cast<const unsigned char*>(Vh) + off), 0, (int)bytes,
+            0x00020000);
+        const int sl = lane + u * 64;
+        const int row = sl / G_::CPR;
+        const int chunk = (sl % G_::CPR) ^ G_::swz(row);
+        const int vo = (int)((uint32_t)(row - u * RPU) * kpitch + (uint32_t)(chunk << 4));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LDS_PTR(void, tile_ptr(buf, 0) + u * 1024), 16,
+                                                 vo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LDS_PTR(void, tile_ptr(buf, 1) + u * 1024), 16,
+                                                 vo, 0, 0, 0);
+      }
+      if (buf == 0) absent0 = absent; else absent1 = absent;
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < NSLOT / 64; ++u) {
       const int sl = lane + u * 64;
@@ -146,10 +231,12 @@ __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
     }
   };
 
-  // One 64-key tile: the split's keys past k1 (and Nk) and, when causal,
-  // keys past the row's diagonal are masked.
+  // One 64-key tile: the split's keys past k1 (and Nk), when causal keys
+  // past the row's diagonal, keys below the row's window and keys of absent
+  // pages are masked.
   auto compute = [&](auto bufc, int j0) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
+    const uint64_t absent = PAGED ? (buf == 0 ? absent0 : absent1) : 0;
     const unsigned char* kt = tile_ptr(buf, 0);
     const unsigned char* vt = tile_ptr(buf, 1);
     constexpr int NS = (BN / 32) * KC;
@@ -184,15 +271,21 @@ __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
     for (int i = 0; i < kVPF && i < NV; ++i) vf[i] = vread(i);
     __builtin_amdgcn_sched_barrier(0);
 
-    if ((j0 + BN > k1) || (CAUSAL && j0 + BN - 1 > off)) {
-      // Register r of block mb holds key j0 + 4*h32 + kr, kr = 32mb + 8(r/4) + r%4.
+    if ((j0 + BN > k1) || (CAUSAL && j0 + BN - 1 > off) || (win > 0 && j0 <= Nq - 1 + off - win) ||
+        (PAGED && absent != 0)) {
+      // Register r of block mb holds key j0 + 4*h32 + kr, kr = 32mb + 8(r/4) + r%4:
+      // visible iff wlo < kr < lim and its page is present.
       const int lim = min(k1 - j0, CAUSAL ? qi + off - j0 + 1 : k1 - j0) - 4 * h32;
+      const int wlo = win > 0 ? qi + off - win - j0 - 4 * h32 : -(1 << 30);
+      const uint64_t present = ~(absent >> (4 * h32));
 #pragma unroll
       for (int mb = 0; mb < BN / 32; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kr = mb * 32 + (r >> 2) * 8 + (r & 3);
-          s[mb][r] = kr < lim ? s[mb][r] : kNegInf;
+          bool vis = kr < lim && kr > wlo;
+          if (PAGED) vis = vis && ((present >> kr) & 1ull);
+          s[mb][r] = vis ? s[mb][r] : kNegInf;
         }
     }
     float mx = s[0][0];
@@ -242,15 +335,21 @@ __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
   // waiting for its own loads, so the next step's reads never wait on the
   // tile it puts in flight.
   constexpr int kWaitLoads = 0x0F70;  // s_waitcnt vmcnt(0)
+  // Paged: the page entries of the next tile to load are fetched one step
+  // ahead and arrive with that step's wait.
   if (t0 + wave < t1) {
-    load_tile(t0 + wave, std::integral_constant<int, 0>{});
+    int pv = fetch_pages(t0 + wave);
+    load_tile(t0 + wave, std::integral_constant<int, 0>{}, pv);
+    pv = fetch_pages(t0 + wave + KS);
     __builtin_amdgcn_s_waitcnt(kWaitLoads);
     for (int t = t0 + wave; t < t1; t += 2 * KS) {
-      if (t + KS < t1) load_tile(t + KS, std::integral_constant<int, 1>{});
+      if (t + KS < t1) load_tile(t + KS, std::integral_constant<int, 1>{}, pv);
+      pv = fetch_pages(t + 2 * KS);
       compute(std::integral_constant<int, 0>{}, t * BN);
       __builtin_amdgcn_s_waitcnt(kWaitLoads);
       if (t + KS < t1) {
-        if (t + 2 * KS < t1) load_tile(t + 2 * KS, std::integral_constant<int, 0>{});
+        if (t + 2 * KS < t1) load_tile(t + 2 * KS, std::integral_constant<int, 0>{}, pv);
+        pv = fetch_pages(t + 3 * KS);
         compute(std::integral_constant<int, 1>{}, (t + KS) * BN);
         __builtin_amdgcn_s_waitcnt(kWaitLoads);
       }
@@ -315,7 +414,7 @@ __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
   }
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool PAGED>
 hipError_t launch_typed(const Problem& p, const DecodePlan& plan, float* scratch) {
   GqaArgs a;
   a.q = p.q;
@@ -330,18 +429,35 @@ hipError_t launch_typed(const Problem& p, const DecodePlan& plan, float* scratch
   a.S = plan.splits;
   a.kps = plan.keys_per_split;
   a.c = p.scale * kLog2e;
-  hipLaunchKernelGGL((decode_gqa_kernel<T, D, CAUSAL>), dim3((unsigned)(p.B * p.Hkv), plan.splits),
+  a.window = (int)p.window;
+  a.table = p.table;
+  a.lens = p.lens;
+  a.max_pages = (int)p.max_pages;
+  a.page_shift = 0;
+  while ((int64_t(1) << a.page_shift) < p.page_size) ++a.page_shift;
+  // Entries at or past 2^31 pages cannot be stored in the int32 table.
+  a.num_pages = (int)(p.num_pages < INT32_MAX ? p.num_pages : INT32_MAX);
+  hipLaunchKernelGGL((decode_gqa_kernel<T, D, CAUSAL, PAGED>), dim3((unsigned)(p.B * p.Hkv), plan.splits),
                      dim3(kWaves<D> * 64), 0, p.stream, a);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_d(const Problem& p, const DecodePlan& plan, float* scratch) {
+  if (p.table)
+    return p.causal ? launch_typed<T, D, true, true>(p, plan, scratch)
+                    : launch_typed<T, D, false, true>(p, plan, scratch);
+  return p.causal ? launch_typed<T, D, true, false>(p, plan, scratch)
+                  : launch_typed<T, D, false, false>(p, plan, scratch);
 }
 
 template <typename T>
 hipError_t launch_t(const Problem& p, const DecodePlan& plan, float* scratch) {
   switch (p.D) {
-    case 16: return p.causal ? launch_typed<T, 16, true>(p, plan, scratch) : launch_typed<T, 16, false>(p, plan, scratch);
-    case 32: return p.causal ? launch_typed<T, 32, true>(p, plan, scratch) : launch_typed<T, 32, false>(p, plan, scratch);
-    case 64: return p.causal ? launch_typed<T, 64, true>(p, plan, scratch) : launch_typed<T, 64, false>(p, plan, scratch);
-    case 128: return p.causal ? launch_typed<T, 128, true>(p, plan, scratch) : launch_typed<T, 128, false>(p, plan, scratch);
+    case 16: return launch_d<T, 16>(p, plan, scratch);
+    case 32: return launch_d<T, 32>(p, plan, scratch);
+    case 64: return launch_d<T, 64>(p, plan, scratch);
+    case 128: return launch_d<T, 128>(p, plan, scratch);
     default: return hipErrorInvalidValue;
   }
 }

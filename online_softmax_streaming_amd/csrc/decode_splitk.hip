@@ -299,25 +299,37 @@ hipError_t launch_t(const Problem& p, const DecodePlan& plan, float* scratch) {
 
 }  // namespace
 
-// Grouped K/V heads, contiguous K/V, no window, bf16/f16, and the G * Nq
-// rows of a K/V head fit one matrix tile: the partial states come from the
-// matrix-core kernel of decode_gqa.hip, which reads each K/V tile once per
-// group.  Its workgroups are (b, K/V head, split): aim for >= 1024 of them
-// with >= 2 tiles per wave in each split.
-DecodePlan plan_decode_gqa(const Problem& p) {
+// Grouped K/V heads, bf16/f16, the G * Nq rows of a K/V head fit one matrix
+// tile, and (paged) a page holds at least the 512 / D rows of one 16-byte
+// load instruction: the partial states come from the matrix-core kernel of
+// decode_gqa.hip, which reads each K/V tile once per group.  Its workgroups
+// are (b, K/V head, split): aim for >= 1024 of them with >= 2 tiles per wave
+// in each split.  The splits cover the longest key range a group can need:
+// the whole sequence, or with a window the keys from row 0's lower bound
+// (rounded down to a 64-key tile) to the end.
+static bool decode_gqa_eligible(const Problem& p) {
+  if (p.dtype != DType::BF16 && p.dtype != DType::F16) return false;
+  if (p.Hkv <= 0 || p.H / p.Hkv <= 1 || (p.H / p.Hkv) * p.Nq > 32) return false;
+  if (p.table && p.page_size < 512 / p.D) return false;
+  return true;
+}
+
+static DecodePlan plan_decode_gqa(const Problem& p) {
   const int64_t kv_rows = p.B * p.Hkv;
   const int64_t waves = p.D > 64 ? 2 : 4;
+  int64_t range = p.table ? p.max_pages * p.page_size : p.Nk;
+  if (p.window > 0 && p.window + p.Nq + 62 < range) range = p.window + p.Nq + 62;
   const int64_t want = (1024 + kv_rows - 1) / kv_rows;
-  int64_t kps = (p.Nk + want - 1) / want;
+  int64_t kps = (range + want - 1) / want;
   const int64_t min_kps = 64 * waves * 2;
   if (kps < min_kps) kps = min_kps;
   kps = (kps + 63) / 64 * 64;
-  int64_t splits = (p.Nk + kps - 1) / kps;
+  int64_t splits = (range + kps - 1) / kps;
   if (splits < 1) splits = 1;
   if (splits > 65535) {
     splits = 65535;
-    kps = ((p.Nk + splits - 1) / splits + 63) / 64 * 64;
-    splits = (p.Nk + kps - 1) / kps;
+    kps = ((range + splits - 1) / splits + 63) / 64 * 64;
+    splits = (range + kps - 1) / kps;
   }
   DecodePlan plan;
   plan.splits = (int)splits;
@@ -328,9 +340,7 @@ DecodePlan plan_decode_gqa(const Problem& p) {
 }
 
 DecodePlan plan_decode(const Problem& p) {
-  if (!p.table && p.window == 0 && (p.dtype == DType::BF16 || p.dtype == DType::F16) &&
-      p.Hkv > 0 && p.H / p.Hkv > 1 && (p.H / p.Hkv) * p.Nq <= 32)
-    return plan_decode_gqa(p);
+  if (decode_gqa_eligible(p)) return plan_decode_gqa(p);
   // Aim for >= 4096 workgroups (16 per CU) so the HBM stream is deep enough,
   // but give each split at least 256 keys so the merge stays cheap.  The
   // splits cover the longest visible key range a row can have.

@@ -60,6 +60,15 @@ def _check(lib, inputs, causal, window, dtype, batches=None):
     (4, 4, 4, 64, 64, [2, 5, 130, 700]),    # causal: a sequence shorter than Nq
     (2, 1, 2, 32, 1, [1, 17, 64]),
     (4, 2, 8, 16, 32, [9, 200]),
+    # Grouped heads on the matrix-core path: pages of 64 and 256 keys (one
+    # page per 64-key tile or several tiles per page), 8-key pages (eight
+    # pages per tile), 32 packed rows, and 2-key pages at D = 64 (below the
+    # 8 rows of one load: the row-streaming path).
+    (16, 2, 1, 128, 64, [1, 63, 64, 65, 2000]),
+    (32, 1, 1, 64, 256, [300, 1, 1025]),
+    (8, 2, 4, 128, 8, [4, 5, 77, 1500]),
+    (12, 3, 8, 32, 16, [8, 9, 700]),
+    (8, 4, 1, 64, 2, [3, 130]),
 ])
 def test_parity(lib, dtype, causal, h, hkv, nq, d, page, lens):
     inputs = make_paged(len(lens), h, hkv, nq, d, page, lens, dtype, seed=h + nq + d + page,
@@ -73,6 +82,15 @@ def test_sliding_window(lib, dtype, window, nq):
     inputs = make_paged(3, 4, 2, nq, 128, 16, [1000, 4096, 50], dtype, seed=window + nq,
                         device="cuda")
     _check(lib, inputs, True, window, dtype)
+
+
+@pytest.mark.parametrize("window,nq,page", [(64, 1, 64), (65, 2, 32), (1000, 4, 16), (5000, 1, 128)])
+def test_sliding_window_grouped(lib, window, nq, page):
+    # Eight query heads per K/V head: the splits start at the window's lower
+    # bound rounded down to a 64-key tile.
+    inputs = make_paged(3, 16, 2, nq, 128, page, [1000, 4096, 50], "bf16", seed=window + page,
+                        device="cuda")
+    _check(lib, inputs, True, window, "bf16")
 
 
 def test_window_one_returns_the_last_value(lib):
@@ -102,6 +120,42 @@ def test_absent_pages_contribute_nothing(lib):
     for h in range(2):
         want, _, _ = oracle.attention_rows(_np(q)[0, h], k[h], v[h], False, scale)
         assert np.max(np.abs(_np(out)[0, h] - want)) <= TOL["f16"]
+
+
+@pytest.mark.parametrize("page", [16, 64])
+def test_absent_pages_contribute_nothing_grouped(lib, page):
+    # Grouped heads (four query heads per K/V head, two query rows): an
+    # absent page inside a 64-key tile (page 16) or a whole absent tile
+    # (page 64) masks exactly its keys.
+    npg = 4
+    q, kc, vc, table, lens = make_paged(1, 8, 2, 2, 64, page, [npg * page], "bf16", seed=14,
+                                        device="cuda")
+    bad = table.clone()
+    bad[0, 1] = 1 << 20
+    bad[0, 2] = -7
+    out, _, _ = lib.attn_decode_paged(q, kc, vc, bad, lens, causal=False)
+    torch.cuda.synchronize()
+    keep = [0, 3]
+    k = np.concatenate([_np(kc)[int(table[0, p])] for p in keep], axis=1)
+    v = np.concatenate([_np(vc)[int(table[0, p])] for p in keep], axis=1)
+    scale = lib.default_scale(64)
+    for h in range(8):
+        want, _, _ = oracle.attention_rows(_np(q)[0, h], k[h // 4], v[h // 4], False, scale)
+        assert np.max(np.abs(_np(out)[0, h] - want)) <= TOL["bf16"], h
+
+
+def test_window_one_returns_the_last_value_grouped(lib):
+    # One visible key per row: weight exactly 1 on the matrix-core path too.
+    q, kc, vc, table, lens = make_paged(2, 8, 2, 1, 128, 16, [33, 3000], "bf16", seed=15,
+                                        device="cuda")
+    out, _, l = lib.attn_decode_paged(q, kc, vc, table, lens, causal=True, window=1, want_stats=True)
+    torch.cuda.synchronize()
+    for b, n in enumerate((33, 3000)):
+        j = n - 1
+        page = int(table[b, j // 16])
+        for h in range(8):
+            assert torch.equal(out[b, h, 0], vc[page, h // 4, j % 16]), (b, h)
+        assert torch.all(l[b] == 1.0)
 
 
 def test_unused_table_entries_are_not_read(lib):

@@ -42,6 +42,9 @@ def _grouped(b, h, hkv, nq, nk, d, dtype, seed):
     # tile (up to 32), several key splits, ragged and causal key ends
     (32, 8, 4, 5000, 128), (16, 1, 2, 3001, 64), (32, 1, 1, 2049, 32), (8, 2, 3, 4099, 16),
     (12, 3, 8, 777, 128),
+    # fewer keys than query rows (causal: rows 0 .. Nq - Nk - 1 see no key),
+    # and a single key
+    (8, 2, 6, 2, 64), (16, 2, 2, 1, 128),
     # more than 32 rows per K/V head: the per-row split path
     (8, 1, 5, 1500, 64),
 ])

@@ -69,6 +69,7 @@ def _check(lib, inputs, causal, window, dtype, batches=None):
     (8, 2, 4, 128, 8, [4, 5, 77, 1500]),
     (12, 3, 8, 32, 16, [8, 9, 700]),
     (8, 4, 1, 64, 2, [3, 130]),
+    (8, 2, 4, 64, 16, [2, 3, 600]),         # causal: rows that see no key at all
 ])
 def test_parity(lib, dtype, causal, h, hkv, nq, d, page, lens):
     inputs = make_paged(len(lens), h, hkv, nq, d, page, lens, dtype, seed=h + nq + d + page,

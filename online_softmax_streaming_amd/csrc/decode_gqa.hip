@@ -4,12 +4,15 @@
 //
 // With grouped heads the G query heads of a K/V head read the same keys.
 // Streaming them row by row (the vector-ALU partial kernel in
-// decode_splitk.hip) reads every K/V byte G * Nq times.  Here the G * Nq <= 32
-// query rows that share a K/V head are packed into the 32 columns of one
-// matrix tile (lane l32 holds packed row r = g * Nq + i: head h0 + g, query
-// i), so each K/V tile is read once per group and feeds S = K Q^T and
-// O += P V on the matrix cores.  Workgroup (b, K/V head, split s) covers
-// keys [s * kps, (s + 1) * kps); its KS waves take the 64-key tiles of that
+// decode_splitk.hip) reads every K/V byte G * Nq times.  Here the G * Nq
+// query rows that share a K/V head are packed, 32 at a time, into the 32
+// columns of one matrix tile (packed row r = g * Nq + i is query head
+// h0 + g, query i; chunk z of a group holds rows 32z .. 32z + 31, lane l32
+// row 32z + l32), so each K/V tile is read once per chunk, ceil(G * Nq / 32)
+// times in all, and feeds S = K Q^T and O += P V on the matrix cores.
+// Work item (b, K/V head, split s) with row chunk z covers
+// keys [kbeg + s * kps, kbeg + (s + 1) * kps) (kbeg = 0 unless a sliding
+// window hides the first keys from every row); its KS waves take the 64-key tiles of that
 // range in turn through their own double-buffered LDS tiles, keep the
 // running state of the streaming method per row (answer-key page, row A3),
 // merge their states in LDS (row A1) and write the split's (m, l, a) per
@@ -48,6 +51,8 @@ struct GqaArgs {
   int H, Hkv, G, Nq, Nk;
   int S;        // splits per row
   int kps;      // keys per split (a multiple of 64)
+  int chunks;   // ceil(G * Nq / 32) row chunks per K/V head
+  int nwork;    // B * Hkv * S work items
   float c;      // scale * log2(e)
   int window;   // 0: none
   // Paged cache (PAGED kernels only): sequence b's key j is row j % page_size
@@ -95,8 +100,18 @@ __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
     return buf == 0 ? &buf0[wave][kv][0] : &buf1[wave][kv][0];
   };
 
-  const int split = blockIdx.y;
-  const int bk = blockIdx.x;  // b * Hkv + K/V head
+  // Block -> work item w = (b * Hkv + K/V head) * S + split and row chunk
+  // z.  Blocks are dealt to the 8 XCDs round-robin; the chunks of one work
+  // item are 8 blocks apart, so they run on one XCD close together in time
+  // and the later ones find the K/V tiles in that XCD's L2.
+  const int blk = blockIdx.x;
+  const int xcd = blk & 7;
+  const int r8 = blk >> 3;
+  const int chunk = r8 % a.chunks;  // 32 packed rows of the group
+  const int w = (r8 / a.chunks) * 8 + xcd;
+  if (w >= a.nwork) return;
+  const int split = w % a.S;
+  const int bk = w / a.S;  // b * Hkv + K/V head
   const int b = bk / a.Hkv, hk = bk - b * a.Hkv;
   const int Nq = a.Nq;
   int Nk = a.Nk;
@@ -110,9 +125,10 @@ __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
   const int l32 = lane & 31;
   // Packed row of this lane: query head hk*G + g, query row i.
   const int R = a.G * Nq;
-  const bool real = l32 < R;
-  const int g = real ? l32 / Nq : 0;
-  const int qi = real ? l32 - g * Nq : 0;
+  const int pr = chunk * 32 + l32;
+  const bool real = pr < R;
+  const int g = real ? pr / Nq : 0;
+  const int qi = real ? pr - g * Nq : 0;
   const int64_t qrow = ((int64_t)b * a.H + (int64_t)hk * a.G + g) * Nq + qi;  // row of [B, H, Nq]
   const T* Kh = static_cast<const T*>(a.k) + (PAGED ? 0 : (int64_t)bk * Nk * D);
   const T* Vh = static_cast<const T*>(a.v) + (PAGED ? 0 : (int64_t)bk * Nk * D);
@@ -135,7 +151,9 @@ __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
   const int t1 = k1 > k0 ? (k1 + BN - 1) / BN : t0;  // tiles [t0, t1) of this split
 
   const uint32_t kpitch = (uint32_t)(2 * D);
-  const uint32_t kv_bytes = (uint32_t)Nk * (uint32_t)(2 * D);
+  // Contiguous K/V: one descriptor over the head (fewer than 2^31 elements,
+  // so its byte size fits 32 bits); rows past Nk read as zeros.
+  const uint32_t kv_bytes = PAGED ? 0u : (uint32_t)Nk * (uint32_t)(2 * D);
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(Kh), 0, (int)kv_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -437,7 +455,10 @@ hipError_t launch_typed(const Problem& p, const DecodePlan& plan, float* scratch
   while ((int64_t(1) << a.page_shift) < p.page_size) ++a.page_shift;
   // Entries at or past 2^31 pages cannot be stored in the int32 table.
   a.num_pages = (int)(p.num_pages < INT32_MAX ? p.num_pages : INT32_MAX);
-  hipLaunchKernelGGL((decode_gqa_kernel<T, D, CAUSAL, PAGED>), dim3((unsigned)(p.B * p.Hkv), plan.splits),
+  a.chunks = (int)((a.G * p.Nq + 31) / 32);
+  a.nwork = (int)(p.B * p.Hkv * plan.splits);
+  const int64_t blocks = (int64_t)(a.nwork + 7) / 8 * 8 * a.chunks;
+  hipLaunchKernelGGL((decode_gqa_kernel<T, D, CAUSAL, PAGED>), dim3((unsigned)blocks),
                      dim3(kWaves<D> * 64), 0, p.stream, a);
   return hipGetLastError();
 }

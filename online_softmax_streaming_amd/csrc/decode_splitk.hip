@@ -30,6 +30,8 @@
 // clamped to [0, max_pages * page_size]: table values are never used to
 // address memory outside the cache.
 
+#include <cstdint>
+
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -299,23 +301,23 @@ hipError_t launch_t(const Problem& p, const DecodePlan& plan, float* scratch) {
 
 }  // namespace
 
-// Grouped K/V heads, bf16/f16, the G * Nq rows of a K/V head fit one matrix
-// tile, and (paged) a page holds at least the 512 / D rows of one 16-byte
-// load instruction: the partial states come from the matrix-core kernel of
-// decode_gqa.hip, which reads each K/V tile once per group.  Its workgroups
-// are (b, K/V head, split): aim for >= 1024 of them with >= 2 tiles per wave
-// in each split.  The splits cover the longest key range a group can need:
+// Grouped K/V heads, bf16/f16, and (paged) a page holds at least the 512 / D
+// rows of one 16-byte load instruction: the partial states come from the
+// matrix-core kernel of decode_gqa.hip, which reads each K/V tile once per 32
+// of the group's G * Nq query rows.  Its workgroups are (b, K/V head, split,
+// chunk of 32 rows): aim for >= 1024 of them with >= 2 tiles per wave in each
+// split.  The splits cover the longest key range a group can need:
 // the whole sequence, or with a window the keys from row 0's lower bound
 // (rounded down to a 64-key tile) to the end.
 static bool decode_gqa_eligible(const Problem& p) {
   if (p.dtype != DType::BF16 && p.dtype != DType::F16) return false;
-  if (p.Hkv <= 0 || p.H / p.Hkv <= 1 || (p.H / p.Hkv) * p.Nq > 32) return false;
+  if (p.Hkv <= 0 || p.H / p.Hkv <= 1) return false;
   if (p.table && p.page_size < 512 / p.D) return false;
   return true;
 }
 
 static DecodePlan plan_decode_gqa(const Problem& p) {
-  const int64_t kv_rows = p.B * p.Hkv;
+  const int64_t kv_rows = p.B * p.Hkv * (((p.H / p.Hkv) * p.Nq + 31) / 32);
   const int64_t waves = p.D > 64 ? 2 : 4;
   int64_t range = p.table ? p.max_pages * p.page_size : p.Nk;
   if (p.window > 0 && p.window + p.Nq + 62 < range) range = p.window + p.Nq + 62;
@@ -340,7 +342,13 @@ static DecodePlan plan_decode_gqa(const Problem& p) {
 }
 
 DecodePlan plan_decode(const Problem& p) {
-  if (decode_gqa_eligible(p)) return plan_decode_gqa(p);
+  if (decode_gqa_eligible(p)) {
+    // One block per (work item, row chunk) in a 1-D grid of int-sized indices.
+    const DecodePlan g = plan_decode_gqa(p);
+    const int64_t chunks = ((p.H / p.Hkv) * p.Nq + 31) / 32;
+    const int64_t work8 = (p.B * p.Hkv * g.splits + 7) / 8 * 8;
+    if (work8 <= INT32_MAX / chunks) return g;
+  }
   // Aim for >= 4096 workgroups (16 per CU) so the HBM stream is deep enough,
   // but give each split at least 256 keys so the merge stays cheap.  The
   // splits cover the longest visible key range a row can have.

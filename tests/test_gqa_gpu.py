@@ -45,8 +45,10 @@ def _grouped(b, h, hkv, nq, nk, d, dtype, seed):
     # fewer keys than query rows (causal: rows 0 .. Nq - Nk - 1 see no key),
     # and a single key
     (8, 2, 6, 2, 64), (16, 2, 2, 1, 128),
-    # more than 32 rows per K/V head: the per-row split path
-    (8, 1, 5, 1500, 64),
+    # more than 32 rows per K/V head: chunks of 32 rows, each reading the
+    # K/V tiles once (MQA with 64 query heads; 64 and 96 packed rows; 40
+    # rows, the second chunk ragged)
+    (64, 1, 1, 3001, 128), (16, 2, 8, 700, 64), (48, 1, 2, 999, 32), (8, 1, 5, 1500, 64),
 ])
 def test_parity(lib, dtype, causal, h, hkv, nq, nk, d):
     q, k, v = _grouped(2, h, hkv, nq, nk, d, dtype, seed=h * 10 + hkv + nq)

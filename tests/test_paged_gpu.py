@@ -70,6 +70,8 @@ def _check(lib, inputs, causal, window, dtype, batches=None):
     (12, 3, 8, 32, 16, [8, 9, 700]),
     (8, 4, 1, 64, 2, [3, 130]),
     (8, 2, 4, 64, 16, [2, 3, 600]),         # causal: rows that see no key at all
+    (64, 1, 1, 128, 16, [1, 777, 3000]),    # one K/V head for 64 query heads: two row chunks
+    (16, 2, 5, 64, 8, [5, 300]),            # 40 rows per K/V head
 ])
 def test_parity(lib, dtype, causal, h, hkv, nq, d, page, lens):
     inputs = make_paged(len(lens), h, hkv, nq, d, page, lens, dtype, seed=h + nq + d + page,

@@ -94,3 +94,27 @@ def test_hkv_equal_h_is_attn_fwd_stats(lib):
     b, bm, bl = lib.attn_fwd_stats(q, k, v, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(am, bm) and torch.equal(al, bl)
+
+
+def test_bench_shape_sampled(lib):
+    # The grouped decode the benchmark times, in its launch configuration:
+    # B16 H32 Hkv4 Nq1 Nk32768 D128 bf16, contiguous K/V, noncausal, inputs
+    # drawn as the benchmark draws them; three (b, h) rows checked.
+    b_, h_, hkv, nk, d = 16, 32, 4, 32768, 128
+    q, _, _ = random_qkv(b_, h_, 1, 1, d, "bf16", seed=0, device="cuda")
+    _, k, v = random_qkv(b_, hkv, 1, nk, d, "bf16", seed=1, device="cuda")
+    scale = lib.default_scale(d)
+    out, m, l = lib.attn_fwd_gqa(q, k, v, scale=scale, want_stats=True)
+    torch.cuda.synchronize()
+
+    def np64(t):
+        return t.cpu().double().numpy()
+
+    for bb, hh in ((0, 0), (7, 13), (15, 31)):
+        hk = hh // (h_ // hkv)
+        want, wm, wl = oracle.attention_rows(np64(q[bb, hh]), np64(k[bb, hk]), np64(v[bb, hk]), False,
+                                             scale)
+        err = float(np.max(np.abs(np64(out[bb, hh]) - want)))
+        assert err <= TOL["bf16"], ((bb, hh), err)
+        lse = np64(m[bb, hh]) + np.log(np64(l[bb, hh]))
+        assert np.max(np.abs(lse - (wm + np.log(wl)))) <= LSE_TOL["bf16"], (bb, hh)

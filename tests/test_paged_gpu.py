@@ -175,3 +175,28 @@ def test_serving_shape_sampled(lib):
     lens = [int(x) for x in rng.integers(1, 8193, size=16)]
     inputs = make_paged(16, 32, 8, 1, 128, 16, lens, "bf16", seed=6, device="cuda")
     _check(lib, inputs, True, 0, "bf16", batches=[0, 15])
+
+
+def test_bench_shape_grouped_sampled(lib):
+    # The paged grouped decode the benchmark times, in its launch
+    # configuration: B16 H32 Hkv4 Nq1, 32768 keys per sequence in shuffled
+    # 16-key pages, D128 bf16, causal; two sequences checked.  The oracle gets
+    # the pages of the checked sequence only (same table order), which is all
+    # it reads.
+    q, kc, vc, table, lens = make_paged(16, 32, 4, 1, 128, 16, [32768] * 16, "bf16", seed=2,
+                                        device="cuda")
+    scale = lib.default_scale(128)
+    out, m, l = lib.attn_decode_paged(q, kc, vc, table, lens, causal=True, scale=scale,
+                                      want_stats=True)
+    torch.cuda.synchronize()
+    npg = 32768 // 16
+    for b in (0, 15):
+        pages = table[b, :npg].long()
+        ksub, vsub = _np(kc[pages]), _np(vc[pages])
+        tsub = np.arange(npg, dtype=np.int32).reshape(1, npg)
+        want, wm, wl = oracle.attention_paged(_np(q)[b:b + 1], ksub, vsub, tsub, _np(lens)[b:b + 1],
+                                              True, scale)
+        err = float(np.max(np.abs(_np(out)[b:b + 1] - want)))
+        assert err <= TOL["bf16"], (b, err)
+        lse = _np(m)[b:b + 1] + np.log(_np(l)[b:b + 1])
+        assert np.max(np.abs(lse - (wm + np.log(wl)))) <= LSE_TOL["bf16"], b

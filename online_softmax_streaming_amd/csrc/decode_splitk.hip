@@ -305,8 +305,8 @@ hipError_t launch_t(const Problem& p, const DecodePlan& plan, float* scratch) {
 // rows of one 16-byte load instruction: the partial states come from the
 // matrix-core kernel of decode_gqa.hip, which reads each K/V tile once per 32
 // of the group's G * Nq query rows.  Its workgroups are (b, K/V head, split,
-// chunk of 32 rows): aim for >= 1024 of them with >= 2 tiles per wave in each
-// split.  The splits cover the longest key range a group can need:
+// chunk of 32 rows): aim for ATTN_GQA_WANT_WGS of them with >= 2 tiles per
+// wave in each split.  The splits cover the longest key range a group can need:
 // the whole sequence, or with a window the keys from row 0's lower bound
 // (rounded down to a 64-key tile) to the end.
 static bool decode_gqa_eligible(const Problem& p) {
@@ -316,12 +316,20 @@ static bool decode_gqa_eligible(const Problem& p) {
   return true;
 }
 
+// Workgroups the grouped decode plan aims for: one per CU (a workgroup's
+// double-buffered tiles take most of a CU's LDS, so 256 run as one round
+// with no tail; 512, 768 and 1024 measured up to 40 % slower); a build-time
+// knob.
+#ifndef ATTN_GQA_WANT_WGS
+#define ATTN_GQA_WANT_WGS 256
+#endif
+
 static DecodePlan plan_decode_gqa(const Problem& p) {
   const int64_t kv_rows = p.B * p.Hkv * (((p.H / p.Hkv) * p.Nq + 31) / 32);
   const int64_t waves = p.D > 64 ? 2 : 4;
   int64_t range = p.table ? p.max_pages * p.page_size : p.Nk;
   if (p.window > 0 && p.window + p.Nq + 62 < range) range = p.window + p.Nq + 62;
-  const int64_t want = (1024 + kv_rows - 1) / kv_rows;
+  const int64_t want = (ATTN_GQA_WANT_WGS + kv_rows - 1) / kv_rows;
   int64_t kps = (range + want - 1) / want;
   const int64_t min_kps = 64 * waves * 2;
   if (kps < min_kps) kps = min_kps;

@@ -290,10 +290,9 @@ ATTN_API int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* 
  * keys ending at the row's diagonal.  A row with no visible key gets out = 0
  * and (m, l) = (-inf, 0).  Keys are split across workgroups and the partial
  * states folded with the A1 merge ([AK] rows A1, A2), as attn_fwd does for
- * Nq <= 8; any Nq >= 1 is accepted.  With grouped heads (H / Hkv > 1, bf16
- * or f16, page_size >= 512 / D) each K/V tile read serves 32 of the
- * (H / Hkv) * Nq query rows of its K/V head; otherwise each row streams its
- * keys.
+ * Nq <= 8; any Nq >= 1 is accepted.  With (H / Hkv) * Nq > 1 query rows
+ * per K/V head (bf16 or f16, page_size >= 512 / D) each K/V tile read serves
+ * 32 of them; otherwise each row streams its keys.
  *
  * Layout: Q and out contiguous [B, H, Nq, D]; K_cache and V_cache contiguous
  * [num_pages, Hkv, page_size, D] (one page of one head is contiguous);

@@ -301,7 +301,8 @@ hipError_t launch_t(const Problem& p, const DecodePlan& plan, float* scratch) {
 
 }  // namespace
 
-// Grouped K/V heads, bf16/f16, and (paged) a page holds at least the 512 / D
+// Two or more query rows per K/V head (grouped heads, or Nq > 1), bf16/f16,
+// and (paged) a page holds at least the 512 / D
 // rows of one 16-byte load instruction: the partial states come from the
 // matrix-core kernel of decode_gqa.hip, which reads each K/V tile once per 32
 // of the group's G * Nq query rows.  Its workgroups are (b, K/V head, split,
@@ -311,7 +312,9 @@ hipError_t launch_t(const Problem& p, const DecodePlan& plan, float* scratch) {
 // (rounded down to a 64-key tile) to the end.
 static bool decode_gqa_eligible(const Problem& p) {
   if (p.dtype != DType::BF16 && p.dtype != DType::F16) return false;
-  if (p.Hkv <= 0 || p.H / p.Hkv <= 1) return false;
+  // One row per K/V head (plain decode) streams its keys on the vector
+  // ALUs at the HBM rate; two or more rows share the matrix tiles.
+  if (p.Hkv <= 0 || (p.H / p.Hkv) * p.Nq <= 1) return false;
   if (p.table && p.page_size < 512 / p.D) return false;
   return true;
 }

@@ -89,9 +89,13 @@ extern "C" {
  *   dtype         ATTN_F32, ATTN_F16 or ATTN_BF16.
  *   stream        hipStream_t the work is queued on.
  *
- * Memory: the prefill path (Nq > 8) allocates nothing.  The split-key
- * decode path (Nq <= 8) needs a scratch array of partial states, taken
- * stream-ordered with hipMallocAsync / hipFreeAsync on `stream`.
+ * Paths: Nq <= 8 takes the split-key decode path (keys split across
+ * workgroups, partial states merged); so does bf16/f16 with Nq <= 32,
+ * (H / Hkv) * Nq <= 64 and Nk >= 8192.  Everything else takes the tiled
+ * prefill kernels.
+ * Memory: the prefill path allocates nothing.  The split-key decode path
+ * needs a scratch array of partial states, taken stream-ordered with
+ * hipMallocAsync / hipFreeAsync on `stream`.
  */
 ATTN_API int attn_fwd(const void* Q, const void* K, const void* V, void* out,
              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,

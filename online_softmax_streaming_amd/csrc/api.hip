@@ -147,7 +147,7 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
     e = attn::launch_fill_empty(p);
     return e == hipSuccess ? ATTN_OK : hip_fail(e, "fill kernel launch");
   }
-  if (Nq <= attn::kDecodeMaxNq && !mask && window == 0 && !dropout) {
+  if (attn::decode_route(p) && !mask && window == 0 && !dropout) {
     const attn::DecodePlan plan = attn::plan_decode(p);
     keep_pool_memory();
     void* scratch = nullptr;

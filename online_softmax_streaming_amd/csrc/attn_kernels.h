@@ -113,7 +113,11 @@ hipError_t launch_prefill_splitk(const Problem& p);
 // same scratch layout.
 hipError_t launch_bwd_f32(const BwdProblem& p, float* scratch);
 
-// Row count above which attn_fwd takes the prefill kernels.
+// Row count up to which attn_fwd always takes the split-key decode path.
 constexpr int64_t kDecodeMaxNq = 8;
+// Whether attn_fwd takes the split-key decode path: Nq <= kDecodeMaxNq, or
+// (bf16/f16) up to 32 rows per head and 64 per K/V head over >= 8192 keys,
+// where reading each K/V tile once per 32 rows beats the prefill kernel.
+bool decode_route(const Problem& p);
 
 }  // namespace attn

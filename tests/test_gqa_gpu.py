@@ -70,6 +70,20 @@ def test_parity(lib, dtype, causal, h, hkv, nq, nk, d):
     assert np.max(np.abs(lse[fin] - wlse[fin]), initial=0.0) <= LSE_TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("h,hkv,nq,nk,d", [
+    (8, 2, 16, 9000, 64), (6, 3, 20, 8192, 32),  # 64 / 40 rows per K/V head: decode route
+    (8, 2, 17, 8192, 128),                       # 68 rows per K/V head: prefill kernels
+])
+def test_decode_route_mid_rows(lib, dtype, causal, h, hkv, nq, nk, d):
+    # 9..32 query rows per head with at most 64 per K/V head over >= 8192
+    # keys take the split-key path on the matrix cores (bf16/f16 only, so
+    # FP32 is not a case here; with these inputs' ramped keys the logits reach
+    # ~130 in base 2, beyond what FP32 scores carry to 1e-5).
+    test_parity(lib, dtype, causal, h, hkv, nq, nk, d)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("nq", [1, 300])
 def test_equals_mha_on_repeated_kv(lib, dtype, nq):

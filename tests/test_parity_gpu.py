@@ -186,6 +186,22 @@ def test_decode_path_full(dtype, causal, nq, nk):
     _record(f"decode {dtype} causal={causal} Nq={nq} Nk={nk}", err, TOL[dtype])
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(9, 8192), (17, 9000), (32, 8193), (33, 8192), (20, 8191)])
+def test_decode_route_mid_rows(dtype, causal, nq, nk):
+    # bf16/f16 with 9..32 rows over >= 8192 keys take the split-key path on
+    # the matrix cores (rows of a head share each K/V tile read); 33 rows,
+    # fewer keys and FP32 take the prefill kernels.  Same oracle either way.
+    _say(f"decode route dtype={dtype} causal={causal} Nq={nq} Nk={nk}")
+    q, k, v = random_qkv(2, 4, nq, nk, 128, dtype, seed=4, device=DEV, k_ramp=0.002)
+    scale = default_scale(128)
+    out, m, l = attn_fwd_stats(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    err = _compare_full(q, k, v, causal, scale, out, TOL[dtype], m, l)
+    _record(f"decode route {dtype} causal={causal} Nq={nq} Nk={nk}", err, TOL[dtype])
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads, in the configuration the benchmark times.
 # ---------------------------------------------------------------------------

@@ -132,3 +132,28 @@ def test_bench_shape_sampled(lib):
         assert err <= TOL["bf16"], ((bb, hh), err)
         lse = np64(m[bb, hh]) + np.log(np64(l[bb, hh]))
         assert np.max(np.abs(lse - (wm + np.log(wl)))) <= LSE_TOL["bf16"], (bb, hh)
+
+
+def test_bench_shape_nq4_sampled(lib):
+    # The multi-row decode the benchmark times: plain heads (B16 H32 Hkv32)
+    # with 4 causal query rows each over 32768 keys, D128 bf16, inputs drawn
+    # as the benchmark draws them; two heads checked.
+    b_, h_, nq, nk, d = 16, 32, 4, 32768, 128
+    q, _, _ = random_qkv(b_, h_, nq, 1, d, "bf16", seed=0, device="cuda")
+    _, k, v = random_qkv(b_, h_, 1, nk, d, "bf16", seed=1, device="cuda")
+    scale = lib.default_scale(d)
+    out, m, l = lib.attn_fwd_gqa(q, k, v, causal=True, scale=scale, want_stats=True)
+    torch.cuda.synchronize()
+
+    def np64(t):
+        return t.cpu().double().numpy()
+
+    for bb, hh in ((0, 0), (15, 31)):
+        want, wm, wl = oracle.attention_rows(np64(q[bb, hh]), np64(k[bb, hh]), np64(v[bb, hh]), True,
+                                             scale)
+        err = float(np.max(np.abs(np64(out[bb, hh]) - want)))
+        assert err <= TOL["bf16"], ((bb, hh), err)
+        lse = np64(m[bb, hh]) + np.log(np64(l[bb, hh]))
+        assert np.max(np.abs(lse - (wm + np.log(wl)))) <= LSE_TOL["bf16"], (bb, hh)
+    del q, k, v, out
+    torch.cuda.empty_cache()

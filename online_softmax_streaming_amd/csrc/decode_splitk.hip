@@ -302,12 +302,12 @@ hipError_t launch_t(const Problem& p, const DecodePlan& plan, float* scratch) {
 }  // namespace
 
 // Two or more query rows per K/V head (grouped heads, or Nq > 1), bf16/f16,
-// and (paged) a page holds at least the 512 / D
-// rows of one 16-byte load instruction: the partial states come from the
-// matrix-core kernel of decode_gqa.hip, which reads each K/V tile once per 32
-// of the group's G * Nq query rows.  Its workgroups are (b, K/V head, split,
-// chunk of 32 rows): aim for ATTN_GQA_WANT_WGS of them with >= 2 tiles per
-// wave in each split.  The splits cover the longest key range a group can need:
+// and (paged) pages of at least the 512 / D rows that one 16-byte load
+// instruction moves: the partial states come from the matrix-core kernel of
+// decode_gqa.hip, which reads each K/V tile once per 32 of the G * Nq query
+// rows of a K/V head.  Its workgroups are (b, K/V head, split, chunk of 32
+// rows): aim for ATTN_GQA_WANT_WGS of them with >= 2 tiles per wave in each
+// split.  The splits cover the longest key range a K/V head's rows can need:
 // the whole sequence, or with a window the keys from row 0's lower bound
 // (rounded down to a 64-key tile) to the end.
 static bool decode_gqa_eligible(const Problem& p) {

@@ -295,8 +295,8 @@ ATTN_API int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* 
  * and (m, l) = (-inf, 0).  Keys are split across workgroups and the partial
  * states folded with the A1 merge ([AK] rows A1, A2), as attn_fwd does for
  * Nq <= 8; any Nq >= 1 is accepted.  With (H / Hkv) * Nq > 1 query rows
- * per K/V head (bf16 or f16, page_size >= 512 / D) each K/V tile read serves
- * 32 of them; otherwise each row streams its keys.
+ * per K/V head (bf16 or f16, any page size) each K/V tile read serves 32 of
+ * them; otherwise each row streams its keys.
  *
  * Layout: Q and out contiguous [B, H, Nq, D]; K_cache and V_cache contiguous
  * [num_pages, Hkv, page_size, D] (one page of one head is contiguous);

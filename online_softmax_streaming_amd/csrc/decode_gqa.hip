@@ -72,7 +72,11 @@ constexpr float kRefreshGap = 8.0f;  // base-2 units, as in prefill_mfma.hip
 template <int D>
 constexpr int kWaves = D > 64 ? 2 : 4;  // per-wave double-buffered tiles fit in LDS
 
-template <typename T, int D, bool CAUSAL, bool PAGED>
+// Rows of one all-zero 16-byte chunk: the source of the per-row paged loads
+// for keys past the sequence's length or in absent pages.
+__device__ uint4 g_zero_chunk;
+
+template <typename T, int D, bool CAUSAL, bool PAGED, bool ROWPAGE>
 __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
   typedef typename Mfma<T>::vec8 vec8;
   typedef typename Mfma<T>::vec2 vec2;
@@ -187,16 +191,51 @@ __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
   // the tile's loads need it.
   constexpr int NU = NSLOT / 64;  // load instructions per tile and K or V
   const int pshift = a.page_shift;
+  // Pages smaller than RPU rows (ROWPAGE): lane i holds the page of row i
+  // of the tile instead.
   auto fetch_pages = [&](int t) __attribute__((always_inline)) -> int {
     if (!PAGED || t >= t1) return -1;
-    const int j = t * BN + lane * RPU;
-    return lane < NU && j < Nk ? trow[j >> pshift] : -1;
+    const int j = ROWPAGE ? t * BN + lane : t * BN + lane * RPU;
+    return (ROWPAGE || lane < NU) && j < Nk ? trow[j >> pshift] : -1;
   };
   // Per tile buffer, the rows whose page is absent (bit r = row r of the
   // tile); rows past the sequence's length are handled by the length.
   uint64_t absent0 = 0, absent1 = 0;
   auto load_tile = [&](int t, auto bufc, int pv) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
+    if (PAGED && ROWPAGE) {
+      // Every lane addresses its own row (any page size): 64-bit addresses,
+      // global loads straight into LDS; rows past the length or in absent
+      // pages read the zero chunk.  Bit i of the absent set is row i.
+      const int ji = t * BN + lane;
+      const bool present_i = pv >= 0 && pv < a.num_pages;
+      const uint64_t absent = __builtin_amdgcn_ballot_w64(ji < Nk && !present_i);
+      const unsigned char* kb = reinterpret_cast<const unsigned char*>(Kh);
+      const unsigned char* vb = reinterpret_cast<const unsigned char*>(Vh);
+      const unsigned char* zero = reinterpret_cast<const unsigned char*>(&g_zero_chunk);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int sl = lane + u * 64;
+        const int row = sl / G_::CPR;
+        const int chunk = (sl % G_::CPR) ^ G_::swz(row);
+        const int pg = __shfl(pv, row);
+        const int j = t * BN + row;
+        const bool ok = j < Nk && pg >= 0 && pg < a.num_pages;
+        const uint64_t off =
+            ok ? (uint64_t)((((int64_t)pg * a.Hkv + hk) << pshift) + (j & ((1 << pshift) - 1))) *
+                         (uint64_t)(2 * D) +
+                     (uint64_t)(chunk << 4)
+               : 0u;
+        __builtin_amdgcn_global_load_lds(
+            (__attribute__((address_space(1))) void*)(ok ? kb + off : zero),
+            LDS_PTR(void, tile_ptr(buf, 0) + u * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (__attribute__((address_space(1))) void*)(ok ? vb + off : zero),
+            LDS_PTR(void, tile_ptr(buf, 1) + u * 1024), 16, 0, 0);
+      }
+      if (buf == 0) absent0 = absent; else absent1 = absent;
+      return;
+    }
     if (PAGED) {
       // Lane u works out instruction u's rows (one page: page_size >= RPU),
       // its byte offset in the cache and how many of its rows exist; each
@@ -432,7 +471,7 @@ __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool PAGED>
+template <typename T, int D, bool CAUSAL, bool PAGED, bool ROWPAGE>
 hipError_t launch_typed(const Problem& p, const DecodePlan& plan, float* scratch) {
   GqaArgs a;
   a.q = p.q;
@@ -458,18 +497,23 @@ hipError_t launch_typed(const Problem& p, const DecodePlan& plan, float* scratch
   a.chunks = (int)((a.G * p.Nq + 31) / 32);
   a.nwork = (int)(p.B * p.Hkv * plan.splits);
   const int64_t blocks = (int64_t)(a.nwork + 7) / 8 * 8 * a.chunks;
-  hipLaunchKernelGGL((decode_gqa_kernel<T, D, CAUSAL, PAGED>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((decode_gqa_kernel<T, D, CAUSAL, PAGED, ROWPAGE>), dim3((unsigned)blocks),
                      dim3(kWaves<D> * 64), 0, p.stream, a);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_d(const Problem& p, const DecodePlan& plan, float* scratch) {
+  // Pages of at least the RPU = 512 / D rows one load instruction moves get
+  // one descriptor per instruction; smaller pages, per-row addresses.
+  if (p.table && p.page_size < 512 / D)
+    return p.causal ? launch_typed<T, D, true, true, true>(p, plan, scratch)
+                    : launch_typed<T, D, false, true, true>(p, plan, scratch);
   if (p.table)
-    return p.causal ? launch_typed<T, D, true, true>(p, plan, scratch)
-                    : launch_typed<T, D, false, true>(p, plan, scratch);
-  return p.causal ? launch_typed<T, D, true, false>(p, plan, scratch)
-                  : launch_typed<T, D, false, false>(p, plan, scratch);
+    return p.causal ? launch_typed<T, D, true, true, false>(p, plan, scratch)
+                    : launch_typed<T, D, false, true, false>(p, plan, scratch);
+  return p.causal ? launch_typed<T, D, true, false, false>(p, plan, scratch)
+                  : launch_typed<T, D, false, false, false>(p, plan, scratch);
 }
 
 template <typename T>

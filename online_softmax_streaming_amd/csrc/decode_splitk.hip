@@ -302,8 +302,7 @@ hipError_t launch_t(const Problem& p, const DecodePlan& plan, float* scratch) {
 }  // namespace
 
 // Two or more query rows per K/V head (grouped heads, or Nq > 1), bf16/f16,
-// and (paged) pages of at least the 512 / D rows that one 16-byte load
-// instruction moves: the partial states come from the matrix-core kernel of
+// any page size: the partial states come from the matrix-core kernel of
 // decode_gqa.hip, which reads each K/V tile once per 32 of the G * Nq query
 // rows of a K/V head.  Its workgroups are (b, K/V head, split, chunk of 32
 // rows): aim for ATTN_GQA_WANT_WGS of them with >= 2 tiles per wave in each
@@ -315,7 +314,6 @@ static bool decode_gqa_eligible(const Problem& p) {
   // One row per K/V head (plain decode) streams its keys on the vector
   // ALUs at the HBM rate; two or more rows share the matrix tiles.
   if (p.Hkv <= 0 || (p.H / p.Hkv) * p.Nq <= 1) return false;
-  if (p.table && p.page_size < 512 / p.D) return false;
   return true;
 }
 

@@ -72,6 +72,8 @@ def _check(lib, inputs, causal, window, dtype, batches=None):
     (8, 2, 4, 64, 16, [2, 3, 600]),         # causal: rows that see no key at all
     (64, 1, 1, 128, 16, [1, 777, 3000]),    # one K/V head for 64 query heads: two row chunks
     (16, 2, 5, 64, 8, [5, 300]),            # 40 rows per K/V head
+    (16, 2, 1, 128, 1, [1, 100, 3000]),     # one-key pages: per-row addresses
+    (8, 2, 3, 32, 4, [7, 1000]),            # pages below the 16 rows of one load
 ])
 def test_parity(lib, dtype, causal, h, hkv, nq, d, page, lens):
     inputs = make_paged(len(lens), h, hkv, nq, d, page, lens, dtype, seed=h + nq + d + page,
@@ -87,7 +89,8 @@ def test_sliding_window(lib, dtype, window, nq):
     _check(lib, inputs, True, window, dtype)
 
 
-@pytest.mark.parametrize("window,nq,page", [(64, 1, 64), (65, 2, 32), (1000, 4, 16), (5000, 1, 128)])
+@pytest.mark.parametrize("window,nq,page", [(64, 1, 64), (65, 2, 32), (1000, 4, 16), (5000, 1, 128),
+                                           (100, 2, 1)])
 def test_sliding_window_grouped(lib, window, nq, page):
     # Eight query heads per K/V head: the splits start at the window's lower
     # bound rounded down to a 64-key tile.
@@ -125,7 +128,7 @@ def test_absent_pages_contribute_nothing(lib):
         assert np.max(np.abs(_np(out)[0, h] - want)) <= TOL["f16"]
 
 
-@pytest.mark.parametrize("page", [16, 64])
+@pytest.mark.parametrize("page", [2, 16, 64])
 def test_absent_pages_contribute_nothing_grouped(lib, page):
     # Grouped heads (four query heads per K/V head, two query rows): an
     # absent page inside a 64-key tile (page 16) or a whole absent tile

@@ -74,7 +74,7 @@ constexpr int kWaves = D > 64 ? 2 : 4;  // per-wave double-buffered tiles fit in
 
 // Rows of one all-zero 16-byte chunk: the source of the per-row paged loads
 // for keys past the sequence's length or in absent pages.
-__device__ uint4 g_zero_chunk;
+__device__ uint4 g_zero_chunk = {0u, 0u, 0u, 0u};  // never written
 
 template <typename T, int D, bool CAUSAL, bool PAGED, bool ROWPAGE>
 __global__ __launch_bounds__(kWaves<D> * 64) void decode_gqa_kernel(GqaArgs a) {

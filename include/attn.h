@@ -379,7 +379,10 @@ ATTN_API int online_merge_batch(const float* m1, const float* l1,
  *       columns; larger N is accepted), M * ceil(N / chunk) < 2^31.
  * chunk: 256, 512, 1024, 2048 or 4096 columns per chunk, or 0 to let the
  *       library choose (the largest that still gives 2048 chunks in all).
- * Values are not scanned: non-finite inputs are outside the contract.
+ * Values are not scanned.  -inf entries are masked positions ([KN]
+ *       gotchas ledger): they get probability 0, and a row whose entries
+ *       are all -inf is written as zeros.  NaN and +inf are outside the
+ *       contract.
  * Scratch: FP32 (m, l) per chunk and per row, 8 * M * (T + 1) bytes with
  *       T = ceil(N / chunk), taken with hipMallocAsync and released with
  *       hipFreeAsync on `stream`.

@@ -95,9 +95,13 @@ __device__ __forceinline__ State chunk_state(const T* __restrict__ xr, int64_t e
         f[i] = to_f32<T>(v[i]);
         mv = fmaxf(mv, f[i]);
       }
+      // A vector of masked (-inf) entries is the empty state (-inf, 0): its
+      // exponents are taken against the pinned reference 0, never
+      // (-inf) - (-inf).
+      const float rv = pinned_ref(mv);
       float lv = 0.f;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) lv += exp2_hw((f[i] - mv) * kLog2e);
+      for (int i = 0; i < VEC; ++i) lv += exp2_hw((f[i] - rv) * kLog2e);
       s = merge(s, State{mv, lv});
     }
   } else {
@@ -156,8 +160,12 @@ __global__ __launch_bounds__(kSmThreads) void softmax_normalise_kernel(SoftmaxAr
   const int chunk = (int)(wg - row * a.T);
   const T* __restrict__ xr = static_cast<const T*>(a.x) + row * a.N;
   T* __restrict__ yr = static_cast<T*>(a.y) + row * a.N;
-  const float m = a.rm[row];
-  const float inv = 1.f / a.rl[row];
+  // A row whose entries are all masked (-inf) has l = 0: it is written as
+  // zeros, its reference pinned at 0 ("Kernel Notes & Checklist", gotchas
+  // ledger: empty rows must not produce NaN).
+  const float m = pinned_ref(a.rm[row]);
+  const float rl = a.rl[row];
+  const float inv = rl > 0.f ? 1.f / rl : 0.f;
   const int64_t e0 = (int64_t)chunk * a.C;
   const int64_t e1 = e0 + a.C < a.N ? e0 + a.C : a.N;
   if (a.vec) {

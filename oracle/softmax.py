@@ -39,8 +39,14 @@ def softmax_rows(x):
     if x.shape[0] == 0:
         return np.zeros_like(x)
     m = x.max(axis=1, keepdims=True)          # pass 1: row maximum
-    e = np.exp(x - m)                         # pass 2: exponentials ...
-    return e / e.sum(axis=1, keepdims=True)   # ... and their sum
+    # Masked entries are -inf: they weigh exp(-inf) = 0.  A row with every
+    # entry masked has no mass at all; its reference is pinned at 0 and it
+    # returns zeros instead of NaN ("Kernel Notes & Checklist", gotchas
+    # ledger: empty rows are pinned so they cannot produce NaN).
+    ref = np.where(np.isneginf(m), 0.0, m)
+    e = np.exp(x - ref)                       # pass 2: exponentials ...
+    s = e.sum(axis=1, keepdims=True)          # ... and their sum
+    return np.divide(e, s, out=np.zeros_like(e), where=s > 0)
 
 
 def num_chunks(n, chunk):
@@ -86,13 +92,15 @@ def split_softmax_model(x, chunk, bugs=()):
         for c in range(t):
             seg = x[r, c * chunk:(c + 1) * chunk]
             mc = seg.max()
-            parts.append((mc, math.fsum(math.exp(v - mc) for v in seg)))
+            ref = 0.0 if mc == NEG_INF else mc  # an all -inf chunk is the empty state
+            parts.append((mc, math.fsum(math.exp(v - ref) for v in seg)))
         if "local_normalise" in bugs:
             for c, (mc, lc) in enumerate(parts):
                 seg = x[r, c * chunk:(c + 1) * chunk]
                 y[r, c * chunk:(c + 1) * chunk] = np.exp(seg - mc) / lc
             continue
         m = max(mc for mc, _ in parts)
-        l = math.fsum(lc * math.exp(mc - m) for mc, lc in parts)
-        y[r] = np.exp(x[r] - m) / l
+        ref = 0.0 if m == NEG_INF else m
+        l = math.fsum(lc * math.exp(mc - ref) for mc, lc in parts)
+        y[r] = np.exp(x[r] - ref) / l if l > 0 else 0.0
     return y

@@ -153,3 +153,31 @@ def test_side_stream(lib):
         y = lib.softmax_rows(x, stream=s)
     s.synchronize()
     _check(x, y)
+
+
+def _masked_inputs(m, n, dtype, seed):
+    """Rows with runs of -inf (masked entries): a masked prefix, a run that
+    straddles 16-byte vectors and chunk edges, scattered single entries, a
+    fully masked row and a row masked everywhere but its last entry."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    x = torch.randn(m, n, generator=g, dtype=torch.float32) * 3.0
+    x[0, : min(n - 1, 300)] = float("-inf")
+    x[1, 5: max(6, n // 2)] = float("-inf")
+    x[2, torch.randperm(n, generator=g)[: n // 3]] = float("-inf")
+    x[3, :] = float("-inf")
+    x[4, :-1] = float("-inf")
+    return x.to(dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("n,chunk", [(4096, 256), (1000, 256), (1001, 512), (777, 256)])
+def test_masked_entries(lib, dtype, n, chunk):
+    # Aligned rows (N * size a multiple of 16) take the vector path, where a
+    # vector of -inf entries must give the empty state; odd N takes the
+    # element path.  A fully masked row is written as zeros.
+    x = _masked_inputs(6, n, DT[dtype], seed=n).cuda()
+    y = lib.softmax_rows(x, chunk=chunk)
+    torch.cuda.synchronize()
+    _check(x, y)
+    assert torch.equal(y[3], torch.zeros_like(y[3]))
+    assert bool((y[x == float("-inf")] == 0).all())

@@ -162,3 +162,39 @@ def test_split_model_catches_local_normalisation():
 def test_split_model_rejects_unknown_bug():
     with pytest.raises(ValueError):
         split_softmax_model(np.zeros((1, 4)), 2, bugs=("nope",))
+
+
+# --------------------------------------------------------------------------
+# Masked entries (-inf): the mass of a row is that of its unmasked entries.
+
+def test_masked_entries_reduce_to_softmax_of_the_rest():
+    # Softmax over a row with -inf entries equals the library softmax of the
+    # finite entries, with exact zeros in the masked places; a row with every
+    # entry masked has no mass and returns zeros (never NaN).
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((4, 40)) * 3.0
+    keep = rng.random((4, 40)) < 0.6
+    keep[:, 7] = True          # at least one finite entry per row
+    x[~keep] = -np.inf
+    x[3, :] = -np.inf          # a fully masked row
+    y = softmax_rows(x)
+    assert np.all(np.isfinite(y))
+    assert np.array_equal(y[~keep], np.zeros(int((~keep).sum())))
+    for r in range(3):
+        assert np.allclose(y[r, keep[r]], scipy.special.softmax(x[r, keep[r]]), rtol=1e-13, atol=0)
+    assert np.array_equal(y[3], np.zeros(40))
+
+
+@pytest.mark.parametrize("chunk", [1, 4, 8, 16])
+def test_split_model_with_masked_chunks(chunk):
+    # Whole chunks of -inf (the empty state in the merge), masked runs that
+    # straddle chunk edges, and a fully masked row.
+    rng = np.random.default_rng(chunk)
+    x = rng.standard_normal((3, 64)) * 2.0
+    x[0, :16] = -np.inf
+    x[1, 5:37] = -np.inf
+    x[2, :] = -np.inf
+    y = split_softmax_model(x, chunk)
+    assert np.all(np.isfinite(y))
+    assert np.allclose(y, softmax_rows(x), rtol=1e-13, atol=0)
+    assert np.array_equal(y[2], np.zeros(64))

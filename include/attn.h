@@ -94,8 +94,10 @@ extern "C" {
  * (H / Hkv) * Nq <= 64 and Nk >= 8192.  Everything else takes the tiled
  * prefill kernels.
  * Memory: the prefill path allocates nothing.  The split-key decode path
- * needs a scratch array of partial states, taken stream-ordered with
- * hipMallocAsync / hipFreeAsync on `stream`.
+ * (both routes above) needs a scratch array of partial states, taken
+ * stream-ordered with hipMallocAsync / hipFreeAsync on `stream`; under HIP
+ * graph capture those become the graph's own allocation nodes.  Callers
+ * that cannot allocate at all use attn_decode_paged_noalloc.
  */
 ATTN_API int attn_fwd(const void* Q, const void* K, const void* V, void* out,
              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
@@ -326,6 +328,40 @@ ATTN_API int attn_decode_paged(const void* Q, const void* K_cache, const void* V
                                int64_t D, int64_t num_pages, int64_t page_size,
                                int64_t max_pages, int causal, int64_t window, float scale,
                                int dtype, float* m_out, float* l_out, void* stream);
+
+/*
+ * attn_decode_paged_noalloc -- attn_decode_paged for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc / hipMallocAsync.  It makes no
+ * allocation of any kind (no hipMalloc, hipMallocAsync, hipFree or
+ * allocating library call).
+ *
+ * Arguments, layout, visibility rules, results and status codes are those
+ * of attn_decode_paged.  The partial states of the key splits go to a fixed
+ * library-owned device buffer of 4 MiB instead of stream-ordered scratch;
+ * each GPU the library runs on holds its own copy until the process ends.
+ * The first call on a device looks up that device's copy (with the device
+ * current; no allocation).  When the usual split plan needs more than
+ * 4 MiB (B*H*Nq*S*(D+2) FP32 values for S splits) fewer splits are taken,
+ * which changes only the order of the FP32 sums (results stay within the
+ * same bounds; with the usual plan they equal attn_decode_paged bit for
+ * bit).  A problem whose single split needs more than 4 MiB, i.e.
+ * B*H*Nq*(D+2)*4 > 4 MiB, returns ATTN_E_UNSUPPORTED before any device
+ * work.
+ * Sharing: every call on one GPU uses the same buffer.  Calls queued on one
+ * stream are ordered and safe; calls that may run at the same time on one
+ * GPU (other streams, other threads, without an ordering event between
+ * them) race on the buffer and give wrong results.  The buffer keeps the
+ * last call's contents; every slot a call reads it writes first, so nothing
+ * needs clearing.
+ */
+ATTN_API int attn_decode_paged_noalloc(const void* Q, const void* K_cache, const void* V_cache,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       void* out, int64_t B, int64_t H, int64_t Hkv,
+                                       int64_t Nq, int64_t D, int64_t num_pages,
+                                       int64_t page_size, int64_t max_pages, int causal,
+                                       int64_t window, float scale, int dtype, float* m_out,
+                                       float* l_out, void* stream);
 
 /*
  * online_merge -- merge two A1 summaries ([AK] row A1 and its worked answer).

@@ -17,6 +17,7 @@ from .attn import (  # noqa: F401
     AttnError,
     attn_bwd,
     attn_decode_paged,
+    attn_decode_paged_noalloc,
     attn_fwd,
     attn_fwd_dropout,
     attn_fwd_gqa,

@@ -33,6 +33,9 @@ SIGNATURES = {
     "attn_decode_paged": (ctypes.c_int, [_c_ptr] * 6 + [_c_i64] * 8 + [ctypes.c_int, _c_i64,
                                                                        ctypes.c_float, ctypes.c_int,
                                                                        _c_ptr, _c_ptr, _c_ptr]),
+    "attn_decode_paged_noalloc": (ctypes.c_int, [_c_ptr] * 6 + [_c_i64] * 8 + [ctypes.c_int, _c_i64,
+                                                                               ctypes.c_float, ctypes.c_int,
+                                                                               _c_ptr, _c_ptr, _c_ptr]),
     "attn_fwd_varlen": (ctypes.c_int, [_c_ptr] * 6 + [_c_i64] * 7 + [ctypes.c_int, ctypes.c_float,
                                                                      ctypes.c_int, _c_ptr, _c_ptr,
                                                                      _c_ptr]),

@@ -20,7 +20,6 @@ _DTYPES = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATT
 #: Query rows per head at or below which attn_fwd takes the split-key decode path.
 DECODE_MAX_NQ = 8
 
-
 class AttnError(RuntimeError):
     """A non-zero status from the library."""
 
@@ -327,9 +326,21 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, caus
     return out, m, l
 
 
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, causal=True,
+                              window=0, scale=None, out=None, m_out=None, l_out=None,
+                              want_stats=False, stream=None):
+    """attn_decode_paged through the entry point that allocates nothing
+    (the key splits' partial states go to a fixed 4 MiB device buffer per
+    GPU; calls that may overlap on one GPU race on it).  Pass ``out`` (and
+    ``m_out``/``l_out``) to keep the call itself free of allocations."""
+    return attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, causal=causal,
+                             window=window, scale=scale, out=out, m_out=m_out, l_out=l_out,
+                             want_stats=want_stats, stream=stream, _entry="attn_decode_paged_noalloc")
+
+
 def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, causal=True, window=0,
                       scale=None, out=None, m_out=None, l_out=None, want_stats=False,
-                      stream=None):
+                      stream=None, _entry="attn_decode_paged"):
     """Attention over a paged K/V cache; returns (out, m, l) (m, l None
     unless ``want_stats``).
 
@@ -375,12 +386,12 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, causal=True, w
         sh = _stream_handle(stream, q.device)
         stats = ((ctypes.c_void_p(m_out.data_ptr()), ctypes.c_void_p(l_out.data_ptr()))
                  if want_stats else (None, None))
-        rc = lib().attn_decode_paged(
+        rc = getattr(lib(), _entry)(
             *(ctypes.c_void_p(t.data_ptr()) for t in (q, k_cache, v_cache, block_table, seq_lens,
                                                       out)),
             b, h, hkv, nq, d, num_pages, page_size, max_pages, int(bool(causal)), int(window),
             float(scale), _DTYPES[q.dtype], *stats, sh)
-    _check(rc, "attn_decode_paged")
+    _check(rc, _entry)
     return out, (m_out if want_stats else None), (l_out if want_stats else None)
 
 

@@ -177,6 +177,145 @@ bool valid_chunk(int64_t c) {
   return c == 0 || c == 256 || c == 512 || c == 1024 || c == 2048 || c == 4096;
 }
 
+// Fixed device buffer for attn_decode_paged_noalloc, for callers that
+// cannot allocate.  Each GPU the library runs on holds its own copy until
+// the process ends.  Host code must never pass the array's name to a
+// kernel or a copy (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, looked up once per device
+// with that device current and kept per device.
+constexpr int64_t kNoallocScratchBytes = int64_t(4) << 20;
+static __device__ __align__(256) unsigned char noalloc_scratch[kNoallocScratchBytes];
+
+int noalloc_scratch_ptr(void** out) {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(ATTN_E_UNSUPPORTED, "device ordinal %d is not below 64", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch));
+    if (es != hipSuccess) return hip_fail(es, "hipGetSymbolAddress of the fixed decode buffer");
+    if (!p) return fail(ATTN_E_HIP, "hipGetSymbolAddress gave a NULL fixed decode buffer");
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return ATTN_OK;
+}
+
+// attn_decode_paged and its variant for callers that cannot allocate
+// (`noalloc`: the partial states go to the fixed buffer instead of
+// stream-ordered scratch).
+int run_paged(const void* Q, const void* K_cache, const void* V_cache,
+              const int32_t* block_table, const int32_t* seq_lens, void* out, int64_t B,
+              int64_t H, int64_t Hkv, int64_t Nq, int64_t D, int64_t num_pages,
+              int64_t page_size, int64_t max_pages, int causal, int64_t window, float scale,
+              int dtype, float* m_out, float* l_out, void* stream, bool noalloc) {
+  g_last_error[0] = '\0';
+  if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_E_INVALID, "dtype %d is not ATTN_F32, ATTN_F16 or ATTN_BF16", dtype);
+  if (causal != 0 && causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1, got %d", causal);
+  if (B < 0 || H < 0 || Nq < 0)
+    return fail(ATTN_E_INVALID, "negative size (B=%lld H=%lld Nq=%lld)", (long long)B,
+                (long long)H, (long long)Nq);
+  if (H > 0 && (Hkv < 1 || Hkv > H || H % Hkv != 0))
+    return fail(ATTN_E_INVALID, "Hkv=%lld must divide H=%lld", (long long)Hkv, (long long)H);
+  if (D <= 0) return fail(ATTN_E_INVALID, "D must be positive, got %lld", (long long)D);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(ATTN_E_INVALID, "scale must be finite and > 0, got %g", (double)scale);
+  if (window < 0) return fail(ATTN_E_INVALID, "window must be >= 0, got %lld", (long long)window);
+  if (window > 0 && causal != 1)
+    return fail(ATTN_E_INVALID, "a sliding window needs causal = 1");
+  if (page_size < 1 || (page_size & (page_size - 1)) != 0 || page_size > (1 << 20))
+    return fail(ATTN_E_INVALID, "page_size must be a power of two in [1, 2^20], got %lld",
+                (long long)page_size);
+  if (num_pages < 1 || max_pages < 1 || num_pages > kI32Max || max_pages * page_size > kI32Max)
+    return fail(ATTN_E_INVALID, "need num_pages >= 1, max_pages >= 1, num_pages < 2^31 and "
+                                "max_pages * page_size < 2^31");
+  if (D != 16 && D != 32 && D != 64 && D != 128)
+    return fail(ATTN_E_UNSUPPORTED, "head size D=%lld not built (16, 32, 64, 128)", (long long)D);
+  if (B > kI32Max || H > kI32Max || Nq > kI32Max || B * H > kI32Max || B * H * Nq > kI32Max ||
+      B > kI32Max / max_pages)
+    return fail(ATTN_E_INVALID, "sizes exceed the 32-bit limits (B*H*Nq, B*max_pages < 2^31)");
+  if (B == 0 || H == 0 || Nq == 0) return ATTN_OK;
+
+  const int64_t elem = dtype == ATTN_F32 ? 4 : 2;
+  if (!Q || !K_cache || !V_cache || !block_table || !seq_lens || !out)
+    return fail(ATTN_E_INVALID, "Q, K_cache, V_cache, block_table, seq_lens and out must be non-NULL");
+  if (!aligned(Q, 16) || !aligned(K_cache, 16) || !aligned(V_cache, 16) || !aligned(out, 16))
+    return fail(ATTN_E_INVALID, "Q, K_cache, V_cache and out must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (m_out && !aligned(m_out, 4)) ||
+      (l_out && !aligned(l_out, 4)))
+    return fail(ATTN_E_INVALID, "block_table, seq_lens, m_out and l_out must be 4-byte aligned");
+  if (num_pages > INT64_MAX / Hkv / page_size / D / elem)
+    return fail(ATTN_E_INVALID, "cache size overflows 64 bits");
+  const int64_t qbytes = B * H * Nq * D * elem;
+  const int64_t cbytes = num_pages * Hkv * page_size * D * elem;
+  const int64_t sbytes = B * H * Nq * 4;
+  if (overlaps(out, qbytes, Q, qbytes) || overlaps(out, qbytes, K_cache, cbytes) ||
+      overlaps(out, qbytes, V_cache, cbytes) || overlaps(out, qbytes, block_table, B * max_pages * 4) ||
+      overlaps(out, qbytes, seq_lens, B * 4))
+    return fail(ATTN_E_INVALID, "out overlaps an input");
+  if (overlaps(m_out, sbytes, out, qbytes) || overlaps(l_out, sbytes, out, qbytes) ||
+      overlaps(m_out, sbytes, l_out, sbytes))
+    return fail(ATTN_E_INVALID, "m_out / l_out overlap out or each other");
+
+  attn::Problem p;
+  p.q = Q;
+  p.k = K_cache;
+  p.v = V_cache;
+  p.o = out;
+  p.m_out = m_out;
+  p.l_out = l_out;
+  p.B = B;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = max_pages * page_size;
+  p.D = D;
+  p.causal = causal != 0;
+  p.scale = scale;
+  p.dtype = static_cast<attn::DType>(dtype);
+  p.stream = static_cast<hipStream_t>(stream);
+  p.window = window;
+  p.table = block_table;
+  p.lens = seq_lens;
+  p.max_pages = max_pages;
+  p.page_size = page_size;
+  p.num_pages = num_pages;
+
+  if (noalloc) {
+    // One key split needs B*H*Nq*(D+2) FP32 values; fewer splits than the
+    // usual plan are taken when that plan does not fit the fixed buffer.
+    const int64_t per_split = B * H * Nq * (D + 2) * 4;
+    if (per_split > kNoallocScratchBytes)
+      return fail(ATTN_E_UNSUPPORTED,
+                  "attn_decode_paged_noalloc: one key split of B*H*Nq=%lld rows needs %lld bytes, "
+                  "the fixed buffer holds %lld",
+                  (long long)(B * H * Nq), (long long)per_split, (long long)kNoallocScratchBytes);
+    void* fixed = nullptr;
+    const int rc = noalloc_scratch_ptr(&fixed);
+    if (rc != ATTN_OK) return rc;
+    const attn::DecodePlan plan = attn::plan_decode(p, kNoallocScratchBytes / per_split);
+    if ((int64_t)plan.scratch_bytes > kNoallocScratchBytes)
+      return fail(ATTN_E_UNSUPPORTED, "attn_decode_paged_noalloc: plan exceeds the fixed buffer");
+    const hipError_t e = attn::launch_decode(p, plan, static_cast<float*>(fixed));
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "paged decode kernel launch");
+  }
+  const attn::DecodePlan plan = attn::plan_decode(p);
+  keep_pool_memory();
+  void* scratch = nullptr;
+  hipError_t e = hipMallocAsync(&scratch, plan.scratch_bytes, p.stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of decode scratch");
+  e = attn::launch_decode(p, plan, static_cast<float*>(scratch));
+  const hipError_t ef = hipFreeAsync(scratch, p.stream);
+  if (e != hipSuccess) return hip_fail(e, "paged decode kernel launch");
+  if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of decode scratch");
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -325,89 +464,20 @@ int attn_decode_paged(const void* Q, const void* K_cache, const void* V_cache,
                       int64_t H, int64_t Hkv, int64_t Nq, int64_t D, int64_t num_pages,
                       int64_t page_size, int64_t max_pages, int causal, int64_t window,
                       float scale, int dtype, float* m_out, float* l_out, void* stream) {
-  g_last_error[0] = '\0';
-  if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16)
-    return fail(ATTN_E_INVALID, "dtype %d is not ATTN_F32, ATTN_F16 or ATTN_BF16", dtype);
-  if (causal != 0 && causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1, got %d", causal);
-  if (B < 0 || H < 0 || Nq < 0)
-    return fail(ATTN_E_INVALID, "negative size (B=%lld H=%lld Nq=%lld)", (long long)B,
-                (long long)H, (long long)Nq);
-  if (H > 0 && (Hkv < 1 || Hkv > H || H % Hkv != 0))
-    return fail(ATTN_E_INVALID, "Hkv=%lld must divide H=%lld", (long long)Hkv, (long long)H);
-  if (D <= 0) return fail(ATTN_E_INVALID, "D must be positive, got %lld", (long long)D);
-  if (!(scale > 0.f) || !isfinite(scale))
-    return fail(ATTN_E_INVALID, "scale must be finite and > 0, got %g", (double)scale);
-  if (window < 0) return fail(ATTN_E_INVALID, "window must be >= 0, got %lld", (long long)window);
-  if (window > 0 && causal != 1)
-    return fail(ATTN_E_INVALID, "a sliding window needs causal = 1");
-  if (page_size < 1 || (page_size & (page_size - 1)) != 0 || page_size > (1 << 20))
-    return fail(ATTN_E_INVALID, "page_size must be a power of two in [1, 2^20], got %lld",
-                (long long)page_size);
-  if (num_pages < 1 || max_pages < 1 || num_pages > kI32Max || max_pages * page_size > kI32Max)
-    return fail(ATTN_E_INVALID, "need num_pages >= 1, max_pages >= 1, num_pages < 2^31 and "
-                                "max_pages * page_size < 2^31");
-  if (D != 16 && D != 32 && D != 64 && D != 128)
-    return fail(ATTN_E_UNSUPPORTED, "head size D=%lld not built (16, 32, 64, 128)", (long long)D);
-  if (B > kI32Max || H > kI32Max || Nq > kI32Max || B * H > kI32Max || B * H * Nq > kI32Max ||
-      B > kI32Max / max_pages)
-    return fail(ATTN_E_INVALID, "sizes exceed the 32-bit limits (B*H*Nq, B*max_pages < 2^31)");
-  if (B == 0 || H == 0 || Nq == 0) return ATTN_OK;
+  return run_paged(Q, K_cache, V_cache, block_table, seq_lens, out, B, H, Hkv, Nq, D, num_pages,
+                   page_size, max_pages, causal, window, scale, dtype, m_out, l_out, stream,
+                   false);
+}
 
-  const int64_t elem = dtype == ATTN_F32 ? 4 : 2;
-  if (!Q || !K_cache || !V_cache || !block_table || !seq_lens || !out)
-    return fail(ATTN_E_INVALID, "Q, K_cache, V_cache, block_table, seq_lens and out must be non-NULL");
-  if (!aligned(Q, 16) || !aligned(K_cache, 16) || !aligned(V_cache, 16) || !aligned(out, 16))
-    return fail(ATTN_E_INVALID, "Q, K_cache, V_cache and out must be 16-byte aligned");
-  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (m_out && !aligned(m_out, 4)) ||
-      (l_out && !aligned(l_out, 4)))
-    return fail(ATTN_E_INVALID, "block_table, seq_lens, m_out and l_out must be 4-byte aligned");
-  if (num_pages > INT64_MAX / Hkv / page_size / D / elem)
-    return fail(ATTN_E_INVALID, "cache size overflows 64 bits");
-  const int64_t qbytes = B * H * Nq * D * elem;
-  const int64_t cbytes = num_pages * Hkv * page_size * D * elem;
-  const int64_t sbytes = B * H * Nq * 4;
-  if (overlaps(out, qbytes, Q, qbytes) || overlaps(out, qbytes, K_cache, cbytes) ||
-      overlaps(out, qbytes, V_cache, cbytes) || overlaps(out, qbytes, block_table, B * max_pages * 4) ||
-      overlaps(out, qbytes, seq_lens, B * 4))
-    return fail(ATTN_E_INVALID, "out overlaps an input");
-  if (overlaps(m_out, sbytes, out, qbytes) || overlaps(l_out, sbytes, out, qbytes) ||
-      overlaps(m_out, sbytes, l_out, sbytes))
-    return fail(ATTN_E_INVALID, "m_out / l_out overlap out or each other");
-
-  attn::Problem p;
-  p.q = Q;
-  p.k = K_cache;
-  p.v = V_cache;
-  p.o = out;
-  p.m_out = m_out;
-  p.l_out = l_out;
-  p.B = B;
-  p.H = H;
-  p.Hkv = Hkv;
-  p.Nq = Nq;
-  p.Nk = max_pages * page_size;
-  p.D = D;
-  p.causal = causal != 0;
-  p.scale = scale;
-  p.dtype = static_cast<attn::DType>(dtype);
-  p.stream = static_cast<hipStream_t>(stream);
-  p.window = window;
-  p.table = block_table;
-  p.lens = seq_lens;
-  p.max_pages = max_pages;
-  p.page_size = page_size;
-  p.num_pages = num_pages;
-
-  const attn::DecodePlan plan = attn::plan_decode(p);
-  keep_pool_memory();
-  void* scratch = nullptr;
-  hipError_t e = hipMallocAsync(&scratch, plan.scratch_bytes, p.stream);
-  if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of decode scratch");
-  e = attn::launch_decode(p, plan, static_cast<float*>(scratch));
-  const hipError_t ef = hipFreeAsync(scratch, p.stream);
-  if (e != hipSuccess) return hip_fail(e, "paged decode kernel launch");
-  if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of decode scratch");
-  return ATTN_OK;
+int attn_decode_paged_noalloc(const void* Q, const void* K_cache, const void* V_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, void* out,
+                              int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t D,
+                              int64_t num_pages, int64_t page_size, int64_t max_pages,
+                              int causal, int64_t window, float scale, int dtype, float* m_out,
+                              float* l_out, void* stream) {
+  return run_paged(Q, K_cache, V_cache, block_table, seq_lens, out, B, H, Hkv, Nq, D, num_pages,
+                   page_size, max_pages, causal, window, scale, dtype, m_out, l_out, stream,
+                   true);
 }
 
 int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* out,

@@ -62,7 +62,9 @@ struct DecodePlan {
   size_t scratch_bytes; // partial (m, l, a[D]) states, FP32
   bool gqa_mfma = false;  // partial states from the grouped-head matrix-core kernel
 };
-DecodePlan plan_decode(const Problem& p);
+// At most `max_splits` key splits (fewer keys per split beyond that are
+// not taken); the grid bounds it at 65535.
+DecodePlan plan_decode(const Problem& p, int64_t max_splits = 65535);
 hipError_t launch_decode(const Problem& p, const DecodePlan& plan, float* scratch);
 // Partial states of the split-key decode for grouped K/V heads on the matrix
 // cores (decode_gqa.hip); plan from plan_decode.

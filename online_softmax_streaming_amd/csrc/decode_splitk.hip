@@ -325,7 +325,7 @@ static bool decode_gqa_eligible(const Problem& p) {
 #define ATTN_GQA_WANT_WGS 256
 #endif
 
-static DecodePlan plan_decode_gqa(const Problem& p) {
+static DecodePlan plan_decode_gqa(const Problem& p, int64_t max_splits) {
   const int64_t kv_rows = p.B * p.Hkv * (((p.H / p.Hkv) * p.Nq + 31) / 32);
   const int64_t waves = p.D > 64 ? 2 : 4;
   int64_t range = p.table ? p.max_pages * p.page_size : p.Nk;
@@ -337,10 +337,11 @@ static DecodePlan plan_decode_gqa(const Problem& p) {
   kps = (kps + 63) / 64 * 64;
   int64_t splits = (range + kps - 1) / kps;
   if (splits < 1) splits = 1;
-  if (splits > 65535) {
-    splits = 65535;
+  if (splits > max_splits) {
+    splits = max_splits;
     kps = ((range + splits - 1) / splits + 63) / 64 * 64;
     splits = (range + kps - 1) / kps;
+    if (splits < 1) splits = 1;
   }
   DecodePlan plan;
   plan.splits = (int)splits;
@@ -361,10 +362,13 @@ bool decode_route(const Problem& p) {
   return p.Nq <= 32 && (p.H / p.Hkv) * p.Nq <= 64 && p.Nk >= 8192;
 }
 
-DecodePlan plan_decode(const Problem& p) {
+DecodePlan plan_decode(const Problem& p, int64_t max_splits) {
+  // The grid's y extent bounds the splits of the row-streaming kernel.
+  if (max_splits > 65535) max_splits = 65535;
+  if (max_splits < 1) max_splits = 1;
   if (decode_gqa_eligible(p)) {
     // One block per (work item, row chunk) in a 1-D grid of int-sized indices.
-    const DecodePlan g = plan_decode_gqa(p);
+    const DecodePlan g = plan_decode_gqa(p, max_splits);
     const int64_t chunks = ((p.H / p.Hkv) * p.Nq + 31) / 32;
     const int64_t work8 = (p.B * p.Hkv * g.splits + 7) / 8 * 8;
     if (work8 <= INT32_MAX / chunks) return g;
@@ -380,9 +384,11 @@ DecodePlan plan_decode(const Problem& p) {
   if (kps < 256) kps = 256;
   int64_t splits = (range + kps - 1) / kps;
   if (splits < 1) splits = 1;
-  if (splits > 65535) {  // grid.y limit
-    splits = 65535;
+  if (splits > max_splits) {
+    splits = max_splits;
     kps = (range + splits - 1) / splits;
+    splits = (range + kps - 1) / kps;
+    if (splits < 1) splits = 1;
   }
   DecodePlan plan;
   plan.splits = (int)splits;

@@ -17,9 +17,6 @@ ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_HIP = 0, 1, 2, 3
 
 _DTYPES = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
 
-#: Query rows per head at or below which attn_fwd takes the split-key decode path.
-DECODE_MAX_NQ = 8
-
 class AttnError(RuntimeError):
     """A non-zero status from the library."""
 

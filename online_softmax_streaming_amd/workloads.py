@@ -6,6 +6,13 @@ tensors.  Recipe: Q, K, V ~ N(0, 1) as float32 from one seeded torch
 generator, drawn in the order Q, K, V, then rounded to the workload's dtype.
 The ragged workload adds ``k_ramp * j`` to every element of key row j (a
 rising key offset pushes the running max up tile after tile).
+
+The generator is torch's CPU generator (``torch.Generator('cpu')``), so the
+same seed gives the same inputs on any machine and a host-side
+re-derivation reproduces what the GPU ran on; the tensors are then copied
+to the target device.  Only tensors of more than HOST_GEN_MAX_ELEMS
+elements (the decode workload's K and V, 2^31 elements each) are drawn on
+the target device's own generator instead.
 """
 
 import dataclasses
@@ -14,6 +21,18 @@ import itertools
 import torch
 
 DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+#: Largest tensor (elements) drawn on the host generator; larger ones are
+#: drawn on the target device's generator.
+HOST_GEN_MAX_ELEMS = 1 << 28
+
+
+def generator_device(largest_elems, device):
+    """Where inputs whose largest tensor has ``largest_elems`` elements are
+    drawn: the host ("cpu") unless that tensor exceeds HOST_GEN_MAX_ELEMS."""
+    if str(device) == "cpu" or largest_elems <= HOST_GEN_MAX_ELEMS:
+        return "cpu"
+    return device
 
 
 @dataclasses.dataclass(frozen=True)
@@ -82,7 +101,7 @@ WORKLOADS = {w.name: w for w in [
 def make_qkv(w, seed=0, device="cpu"):
     """Q, K, V for workload ``w``: N(0, 1) float32 from ``seed``, order Q, K, V,
     key ramp added, then rounded to the workload dtype on ``device``."""
-    gen_device = "cpu" if str(device) == "cpu" else device
+    gen_device = generator_device(w.B * w.H * max(w.Nq, w.Nk) * w.D, device)
     g = torch.Generator(device=gen_device)
     g.manual_seed(seed)
     shape_q = (w.B, w.H, w.Nq, w.D)
@@ -106,7 +125,10 @@ def random_qkv(B, H, Nq, Nk, D, dtype, seed=0, device="cpu", k_ramp=0.0):
 def random_dout(shape, dtype, seed=0, device="cpu"):
     """An upstream gradient dO of ``shape``: N(0, 1) float32 from its own
     generator seeded with ``seed``, rounded to ``dtype`` ("f16", "bf16")."""
-    gen_device = "cpu" if str(device) == "cpu" else device
+    numel = 1
+    for n in shape:
+        numel *= int(n)
+    gen_device = generator_device(numel, device)
     g = torch.Generator(device=gen_device)
     g.manual_seed(seed)
     x = torch.randn(tuple(shape), generator=g, dtype=torch.float32, device=gen_device)
@@ -126,12 +148,12 @@ def make_paged(B, H, Hkv, Nq, D, page_size, seq_lens, dtype, seed=0, device="cpu
     ``share_first_page`` makes sequence 1 reuse sequence 0's first page
     (a shared prefix).
     """
-    gen_device = "cpu" if str(device) == "cpu" else device
-    g = torch.Generator(device=gen_device)
-    g.manual_seed(seed)
     npp = [(int(n) + page_size - 1) // page_size for n in seq_lens]
     max_pages = max(1, max(npp) if npp else 1)
     total = sum(npp) + spare_pages
+    gen_device = generator_device(max(total * Hkv * page_size * D, B * H * Nq * D), device)
+    g = torch.Generator(device=gen_device)
+    g.manual_seed(seed)
     dt = DTYPES[dtype]
     q = torch.randn((B, H, Nq, D), generator=g, dtype=torch.float32, device=gen_device).to(dt)
     kc = torch.randn((total, Hkv, page_size, D), generator=g, dtype=torch.float32,
@@ -155,10 +177,10 @@ def make_varlen(lens_q, lens_k, H, Hkv, D, dtype, seed=0, device="cpu"):
     """Packed variable-length inputs: (q [total_q, H, D], k, v [total_k, Hkv, D],
     cu_q, cu_k int32 [B + 1]); N(0, 1) FP32 from one generator seeded with
     ``seed`` on ``device``, drawn in the order q, k, v, rounded to ``dtype``."""
-    gen_device = "cpu" if str(device) == "cpu" else device
+    tq, tk = int(sum(lens_q)), int(sum(lens_k))
+    gen_device = generator_device(max(tq * H, tk * Hkv) * D, device)
     g = torch.Generator(device=gen_device)
     g.manual_seed(seed)
-    tq, tk = int(sum(lens_q)), int(sum(lens_k))
     dt = DTYPES[dtype]
     q = torch.randn((tq, H, D), generator=g, dtype=torch.float32, device=gen_device).to(dt)
     k = torch.randn((tk, Hkv, D), generator=g, dtype=torch.float32, device=gen_device).to(dt)
@@ -214,8 +236,10 @@ SOFTMAX_WORKLOADS = {w.name: w for w in [
 
 
 def make_softmax_input(w, seed=0, device="cpu"):
-    """x for softmax workload ``w`` from ``seed`` (generated on ``device``)."""
-    g = torch.Generator(device=device)
+    """x for softmax workload ``w`` from ``seed`` (drawn as generator_device
+    says, then placed on ``device``)."""
+    gen_device = generator_device(w.M * w.N, device)
+    g = torch.Generator(device=gen_device)
     g.manual_seed(seed)
-    x = torch.randn((w.M, w.N), generator=g, dtype=torch.float32, device=device) * 3.0
-    return x.to(w.torch_dtype)
+    x = torch.randn((w.M, w.N), generator=g, dtype=torch.float32, device=gen_device) * 3.0
+    return x.to(w.torch_dtype).to(device)

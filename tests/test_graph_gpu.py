@@ -1,8 +1,11 @@
 """The prefill path under HIP graph capture.
 
-With more than 8 query rows attn_fwd and attn_fwd_stats take the tiled
-prefill path, which allocates nothing and launches only kernels on the
-caller's stream, so the calls can be captured into a graph and replayed.  Each
+The shapes here take the tiled prefill path of attn_fwd and attn_fwd_stats
+(more than 8 query rows, and not the bf16/f16 route of up to 32 rows per
+head over 8192 or more keys, which takes the split-key decode path and its
+stream-ordered scratch).  The prefill path allocates nothing and launches
+only kernels on the caller's stream, so the calls can be captured into a
+graph and replayed.  Each
 test captures calls once, replays the graph several times with eager work
 and synchronisations between the replays, and checks every replay bit for
 bit against an eager call on the same inputs (the kernel is deterministic),

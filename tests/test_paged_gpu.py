@@ -74,6 +74,13 @@ def _check(lib, inputs, causal, window, dtype, batches=None):
     (16, 2, 5, 64, 8, [5, 300]),            # 40 rows per K/V head
     (16, 2, 1, 128, 1, [1, 100, 3000]),     # one-key pages: per-row addresses
     (8, 2, 3, 32, 4, [7, 1000]),            # pages below the 16 rows of one load
+    # D = 16: one 16-byte load moves 32 key rows; pages of 1 and 4 keys take
+    # per-row addresses (two loads of 32 rows per tile), 16-key pages too
+    # (below the 32 rows of one load), 32-key pages the descriptor path.
+    (8, 2, 1, 16, 1, [1, 40, 1300]),
+    (8, 2, 2, 16, 4, [3, 65, 999]),
+    (16, 4, 1, 16, 16, [2, 17, 2048]),
+    (4, 1, 4, 16, 32, [1, 100, 700]),
 ])
 def test_parity(lib, dtype, causal, h, hkv, nq, d, page, lens):
     inputs = make_paged(len(lens), h, hkv, nq, d, page, lens, dtype, seed=h + nq + d + page,
@@ -128,13 +135,14 @@ def test_absent_pages_contribute_nothing(lib):
         assert np.max(np.abs(_np(out)[0, h] - want)) <= TOL["f16"]
 
 
-@pytest.mark.parametrize("page", [2, 16, 64])
-def test_absent_pages_contribute_nothing_grouped(lib, page):
+@pytest.mark.parametrize("page,d", [(2, 64), (16, 64), (64, 64), (1, 16), (4, 16), (16, 16)])
+def test_absent_pages_contribute_nothing_grouped(lib, page, d):
     # Grouped heads (four query heads per K/V head, two query rows): an
-    # absent page inside a 64-key tile (page 16) or a whole absent tile
-    # (page 64) masks exactly its keys.
+    # absent page inside a 64-key tile (pages of 1 to 16 keys) or a whole
+    # absent tile (page 64) masks exactly its keys; at D = 16 the per-row
+    # path moves 32 rows per load.
     npg = 4
-    q, kc, vc, table, lens = make_paged(1, 8, 2, 2, 64, page, [npg * page], "bf16", seed=14,
+    q, kc, vc, table, lens = make_paged(1, 8, 2, 2, d, page, [npg * page], "bf16", seed=14,
                                         device="cuda")
     bad = table.clone()
     bad[0, 1] = 1 << 20
@@ -144,7 +152,7 @@ def test_absent_pages_contribute_nothing_grouped(lib, page):
     keep = [0, 3]
     k = np.concatenate([_np(kc)[int(table[0, p])] for p in keep], axis=1)
     v = np.concatenate([_np(vc)[int(table[0, p])] for p in keep], axis=1)
-    scale = lib.default_scale(64)
+    scale = lib.default_scale(d)
     for h in range(8):
         want, _, _ = oracle.attention_rows(_np(q)[0, h], k[h // 4], v[h // 4], False, scale)
         assert np.max(np.abs(_np(out)[0, h] - want)) <= TOL["bf16"], h

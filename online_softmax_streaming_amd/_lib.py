@@ -9,7 +9,10 @@ import ctypes
 import os
 import threading
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# ATTN_LIB_PATH names another build of the same C ABI (the tests' host-only
+# sanitizer build); by default the in-tree library is loaded.
+LIB_PATH = os.environ.get("ATTN_LIB_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 _lock = threading.Lock()
 _lib = None

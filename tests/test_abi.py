@@ -395,3 +395,73 @@ def test_attn_fwd_dropout_rejects_bad_p(attn, p):
     rc = _lib.lib().attn_fwd_dropout(g, 2 * g, 3 * g, 4 * g, 1, 2, 2, 64, 64, 64, 0, 0.125, p, 1, 0,
                                      2, None, None, None)
     assert rc == 1, _lib.lib().attn_last_error()
+
+
+# --------------------------------------------------------------------------
+# Dispatch checks for the host-only sanitizer build (test_host_sanitizer.py):
+# every entry point driven past validation into its path selection, split
+# planning and launch with placeholder device addresses.  They run only
+# against that build, whose HIP stand-ins fail every device call (so each
+# call ends in ATTN_E_HIP and nothing is ever launched); with the real
+# library they are skipped.
+
+_SANITIZER_BUILD = (os.environ.get("ATTN_HOST_SANITIZER") == "1"
+                    and "hostsan" in os.environ.get("ATTN_LIB_PATH", ""))
+sanitizer_only = pytest.mark.skipif(not _SANITIZER_BUILD,
+                                    reason="host-only sanitizer build not loaded")
+
+
+def _ptrs(n):
+    # Well-separated, 16-byte-aligned placeholder addresses (1 TiB apart), so
+    # no overlap check fires; nothing dereferences them in this build.
+    import ctypes
+    return [ctypes.c_void_p((i + 1) << 40) for i in range(n)]
+
+
+@sanitizer_only
+@pytest.mark.parametrize("b,h,nq,nk,d,causal,dtype", [
+    (2, 4, 1024, 1024, 64, 1, 2),      # small: keys split over waves
+    (4, 16, 4096, 4096, 128, 1, 2),    # headline: tiled prefill
+    (3, 8, 4099, 4099, 64, 0, 1),      # ragged fp16
+    (1, 1, 128, 128, 64, 0, 0),        # FP32 vector-ALU prefill
+    (16, 32, 1, 32768, 128, 0, 2),     # decode: split plan + scratch
+    (2, 4, 17, 9000, 128, 1, 2),       # mid-row decode route
+    (2, 4, 5, 0, 32, 1, 2),            # Nk = 0: fill kernel
+])
+def test_dispatch_attn_fwd(attn, b, h, nq, nk, d, causal, dtype):
+    from online_softmax_streaming_amd import _lib
+    q, k, v, o, m, l = _ptrs(6)
+    L = _lib.lib()
+    assert L.attn_fwd(q, k, v, o, b, h, nq, nk, d, causal, 0.125, dtype, None) == attn.ATTN_E_HIP
+    assert L.attn_fwd_stats(q, k, v, o, b, h, nq, nk, d, causal, 0.125, dtype, m, l,
+                            None) == attn.ATTN_E_HIP
+    assert L.attn_fwd_gqa(q, k, v, o, b, h, 1 if h % 2 else 2, nq, nk, d, causal, 0.125, dtype,
+                          m, l, None) == attn.ATTN_E_HIP
+
+
+@sanitizer_only
+def test_dispatch_variants(attn):
+    from online_softmax_streaming_amd import _lib
+    L = _lib.lib()
+    q, k, v, o, m, l, mask, do, dq, dk, dv, t, lens = _ptrs(13)
+    E = attn.ATTN_E_HIP
+    assert L.attn_fwd_masked(q, k, v, o, mask, 1 << 20, 1 << 16, 2, 4, 2, 300, 300, 64, 1, 100,
+                             0.125, 2, m, l, None) == E
+    assert L.attn_fwd_masked(q, k, v, o, None, 0, 0, 2, 4, 4, 300, 300, 64, 1, 100, 0.125, 1,
+                             None, None, None) == E
+    assert L.attn_fwd_dropout(q, k, v, o, 2, 4, 2, 300, 300, 128, 1, 0.125, 0.1, 7, 0, 2, m, l,
+                              None) == E
+    assert L.attn_fwd_varlen(q, k, v, o, t, lens, 4, 8, 2, 5000, 6000, 2000, 64, 1, 0.125, 2, m,
+                             l, None) == E
+    for dtype in (0, 1, 2):
+        assert L.attn_bwd(q, k, v, o, do, m, l, dq, dk, dv, 2, 4, 2, 500, 700, 64, 1, 0.125,
+                          dtype, None) == E
+    for nq, hkv in ((1, 8), (4, 2), (1, 1)):
+        for fn in (L.attn_decode_paged, L.attn_decode_paged_noalloc):
+            assert fn(q, k, v, t, lens, o, 4, 8, hkv, nq, 128, 512, 16, 128, 1, 0, 0.125, 2, m,
+                      l, None) == E
+    assert L.softmax_rows(q, o, 1024, 131072, 0, 2, None) == E
+    assert L.softmax_rows(q, o, 3, 1001, 256, 1, None) == E
+    assert L.softmax_rows_scratch_bytes(4, 32769, 1024) == 1088
+    assert L.online_merge_batch(q, k, v, o, m, l, 1000, None) == E
+    assert b"no device" in L.attn_last_error()

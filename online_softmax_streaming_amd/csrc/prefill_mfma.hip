@@ -199,17 +199,22 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h32 = lane >> 5;
     const int l32 = lane & 31;
-    const int i0 = qt * BM;
+    // Causal: query tiles are aligned to the last row, so when Nq is not a
+    // multiple of BM the partial tile is tile 0, whose rows see the fewest
+    // keys (one key tile at the ragged workload's 3-row tail instead of all
+    // of them); rows i0 .. -1 of that tile are ghosts.
+    const int i0 = qt * BM - (CAUSAL ? (BM - Nq % BM) % BM : 0);
     const int qw0 = i0 + wave * 32;  // first query row of this wave
     const int qrow = qw0 + l32;      // this lane's query row
     const float c = a.c;
 
-    // Q fragment: B operand, 8 consecutive features per k-chunk.  Rows past
-    // Nq (ghost rows) are zero so their scores stay finite; never stored.
+    // Q fragment: B operand, 8 consecutive features per k-chunk.  Rows
+    // outside [0, Nq) (ghost rows) are zero so their scores stay finite;
+    // never stored.
     vec8 qf[KC];
   #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      qf[kc] = qrow < Nq
+      qf[kc] = qrow >= 0 && qrow < Nq
                    ? *reinterpret_cast<const vec8*>(Qh + (int64_t)qrow * sq + kc * 16 + h32 * 8)
                    : vec8{};
     }
@@ -296,7 +301,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
 
     // Mask words of this lane's row for keys j0 .. j0+63 (MASKED only).
     const uint32_t* mrow = nullptr;
-    if (MASKED && a.mask && qrow < Nq) {
+    if (MASKED && a.mask && qrow >= 0 && qrow < Nq) {
       const int b = bh / a.H, h = bh - b * a.H;
       mrow = a.mask + (int64_t)b * a.mask_sb + (int64_t)h * a.mask_sh + (int64_t)qrow * a.mask_words;
     }
@@ -475,7 +480,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
       // wave's rows may see.
       auto wave_active = [&](int u) __attribute__((always_inline)) {
         const int ju = u * BN;
-        bool act = qw0 < Nq && (!CAUSAL || ju <= q_last + off);
+        bool act = qw0 < Nq && qw0 + 31 >= 0 && (!CAUSAL || ju <= q_last + off);
         if (MASKED && win > 0) act = act && ju + BN - 1 > qw0 + off - win;
         return act;
       };
@@ -561,7 +566,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
 
     // Epilogue: join the two half-wave sums, normalise, one cast, store.
     const float l_tot = half_sum(l_run);
-    if (qrow < Nq) {
+    if (qrow >= 0 && qrow < Nq) {
       float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       if (DROPOUT) inv *= a.keep_gain;
       T* orow = Oh + (int64_t)qrow * sq;

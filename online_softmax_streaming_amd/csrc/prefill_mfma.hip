@@ -145,7 +145,12 @@ void prefill_mfma_kernel(PrefillArgs a) {
   // Causal: a workgroup takes query tile nqt-1-r and then tile r of its
   // head, so every workgroup streams the same number of key tiles and the
   // grid fills the CUs evenly (with one tile per workgroup, the short
-  // diagonal tiles at the end of each XCD's range leave CUs idle).
+  // diagonal tiles at the end of each XCD's range leave CUs idle).  The
+  // second pass walks its key tiles from the diagonal down: the head's
+  // workgroups then read key tile x at step x of their first passes and
+  // together at one later step of their second passes, so a tile stays in
+  // L2 between its reads far more often (HBM reads of the B4 H16 N4096
+  // causal workload fall from 1.60 to 1.30 times the algorithmic bytes).
   const int bid = blockIdx.x;
   const int logical = (bid & 7) * a.per_xcd + (bid >> 3);
   if (logical >= a.total) return;
@@ -516,13 +521,17 @@ void prefill_mfma_kernel(PrefillArgs a) {
         need_cur = any_need(t_first & 1);
         need_next = any_need((t_first + 1) & 1);
       }
-      if (need_cur) load_tile(t_first * BN, 0);
+      // Key tile of step t (plain batched causal layout, second pass: from
+      // the diagonal down; every other case in increasing order).
+      const bool down = MODE == kModeBatched && CAUSAL && pass == 1;
+      auto tile_of = [&](int t) __attribute__((always_inline)) { return down ? ntiles - 1 - t : t; };
+      if (need_cur) load_tile(tile_of(t_first) * BN, 0);
       __syncthreads();
       auto step = [&](auto bufc, int t) {
         constexpr int buf = decltype(bufc)::value;
-        const int j0 = t * BN;
+        const int j0 = tile_of(t) * BN;
         const bool more = t + 1 < ntiles;
-        if (more && need_next) load_tile(j0 + BN, buf ^ 1);  // in flight while this tile is computed
+        if (more && need_next) load_tile(tile_of(t + 1) * BN, buf ^ 1);  // in flight while this tile is computed
         const uint32_t mw0 = nw0, mw1 = nw1;
         uint32_t fw0 = 0, fw1 = 0;  // words of tile t+2 (tile skipping only)
         if (MASKED && more) {
@@ -536,7 +545,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
             nw1 = mask_word(j0 / 32 + 3);
           }
         }
-        bool active = need_cur && wave_active(t);
+        bool active = need_cur && wave_active(tile_of(t));
         // A tile none of this wave's rows may see under the mask is skipped.
         if (MASKED && a.mask) active = active && __builtin_amdgcn_ballot_w64((mw0 | mw1) != 0u) != 0;
         if (active) {

@@ -110,8 +110,11 @@ constexpr int kKPF = ATTN_KPF;
 template <int D> constexpr int kVPF = D == 64 ? 2 : ATTN_VPF;
 constexpr float kRefreshGap = 8.0f;  // base-2 units; see the file comment
 
+// Sixteen-wave workgroups (four waves per SIMD) need at most 128 VGPRs.
+template <int NW> constexpr int kWavesPerEu = NW >= 16 ? 4 : 2;
+
 template <typename T, int D, int NW, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<NW>)))
 void prefill_mfma_kernel(PrefillArgs a) {
   constexpr bool VARLEN = MODE == kModeVarlen;
   constexpr bool MASKED = MODE == kModeMasked;
@@ -653,6 +656,7 @@ constexpr int kWaves = ATTN_PREFILL_WAVES;
 // from 64 up, per-workgroup chains are long enough that the eight-wave
 // kernel does (B1 H4 N8192 D128 causal: 192 us here, 258 us split).
 constexpr int64_t kSmallGridWgs = 64;
+constexpr int64_t kNumCUs = 256;
 
 template <typename T, int D>
 hipError_t launch_d(const Problem& p) {
@@ -671,6 +675,16 @@ hipError_t launch_d(const Problem& p) {
   const int64_t nqt = (p.Nq + 32 * kWaves - 1) / (32 * kWaves);
   const int64_t wgs = p.B * p.H * (p.causal ? (nqt + 1) / 2 : nqt);
   if (wgs < kSmallGridWgs) return launch_prefill_splitk(p);
+  if constexpr (D == 64) {
+    // Noncausal D = 64 whose eight-wave grid would put a second workgroup
+    // on some CUs while sixteen-wave workgroups (512 rows) fit one per CU:
+    // the larger workgroups fill the CUs once, each with four waves per SIMD
+    // (B3 H8 N4099 f16: 780 against 730 TFLOP/s; shapes that fill the GPU
+    // several times over are level, small ones lose and keep eight waves).
+    const int64_t wgs16 = p.B * p.H * ((p.Nq + 511) / 512);
+    if (!p.causal && wgs > kNumCUs && wgs16 <= kNumCUs)
+      return launch_typed<T, D, 16, false, kModeBatched>(p);
+  }
   return p.causal ? launch_typed<T, D, kWaves, true, kModeBatched>(p)
                   : launch_typed<T, D, kWaves, false, kModeBatched>(p);
 }

@@ -396,6 +396,26 @@ def test_small_grid_split_and_wide_grid(dtype, causal, nq, nk, d):
                       wl[rep:rep + 1])
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("nq,nk", [(700, 700), (700, 1000), (1000, 333)])
+def test_sixteen_wave_noncausal_d64(dtype, nq, nk):
+    # Noncausal D = 64 with 100 heads of 700-1000 rows: eight-wave
+    # workgroups would number more than the 256 CUs, sixteen-wave ones (512
+    # rows) fit once, so the launch takes the sixteen-wave kernel.  Three
+    # repeats of the two distinct heads are compared in full.
+    _say(f"sixteen-wave D=64 dtype={dtype} Nq={nq} Nk={nk}")
+    q, k, v = random_qkv(1, 2, nq, nk, 64, dtype, seed=nq + nk, device=DEV, k_ramp=0.01)
+    scale = default_scale(64)
+    wide, wm, wl = attn_fwd_stats(q.repeat(50, 1, 1, 1), k.repeat(50, 1, 1, 1),
+                                  v.repeat(50, 1, 1, 1), causal=False, scale=scale)
+    torch.cuda.synchronize()
+    err = 0.0
+    for rep in (0, 23, 49):
+        err = max(err, _compare_full(q, k, v, False, scale, wide[rep:rep + 1], TOL[dtype],
+                                     wm[rep:rep + 1], wl[rep:rep + 1]))
+    _record(f"sixteen-wave {dtype} D=64 Nq={nq} Nk={nk}", err, TOL[dtype])
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("nq,nk,d", [(259, 259, 128), (130, 333, 64), (333, 130, 32),
                                      (100, 100, 16)])

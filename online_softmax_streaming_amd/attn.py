@@ -5,6 +5,7 @@ stream, and every step of the computation runs in the HIP kernels of
 libattn.so.  Nothing here computes attention; there is no CPU path.
 """
 
+import contextlib
 import ctypes
 import math
 
@@ -42,12 +43,43 @@ def default_scale(d):
 
 
 def _stream_handle(stream, device):
+    """The HIP stream to queue on: ``stream``, else torch's current stream of
+    ``device`` (a torch.device or an index)."""
     if stream is None:
-        stream = torch.cuda.current_stream(device)
+        idx = device if isinstance(device, int) else device.index
+        return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(idx))
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+_NO_SWITCH = contextlib.nullcontext()
+
+
+def _on_device(t):
+    """Makes t's GPU current for the call (nothing to do when it already is)."""
+    idx = t.get_device()
+    return _NO_SWITCH if idx == torch.cuda.current_device() else torch.cuda.device(idx)
+
+
 def _validate(q, k, v, grouped=False):
+    # Common case first, with few tensor attribute reads; anything it does
+    # not accept goes through the checks below, which name the problem.
+    try:
+        dt = q.dtype
+        ok = (dt in _DTYPES and dt == k.dtype == v.dtype and q.is_cuda and k.is_cuda
+              and v.is_cuda and q.dim() == 4 and k.dim() == 4 and v.dim() == 4
+              and q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
+              and q.get_device() == k.get_device() == v.get_device())
+    except AttributeError:
+        ok = False
+    if ok:
+        qs, ks = q.shape, k.shape
+        if (ks == v.shape and ks[0] == qs[0] and ks[3] == qs[3]
+                and (ks[1] >= 1 and qs[1] % ks[1] == 0 if grouped else ks[1] == qs[1])):
+            return
+    _validate_slow(q, k, v, grouped)
+
+
+def _validate_slow(q, k, v, grouped):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
@@ -92,8 +124,8 @@ def attn_fwd_stats(q, k, v, causal=False, scale=None, out=None, m_out=None, l_ou
         scale = default_scale(d)
     if out is None:
         out = torch.empty_like(q)
-    elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
-          or not out.is_contiguous()):
+    elif (out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda
+          or out.get_device() != q.get_device() or not out.is_contiguous()):
         raise ValueError("out must be a contiguous tensor like q")
     if want_stats:
         for name, t in (("m_out", m_out), ("l_out", l_out)):
@@ -104,8 +136,8 @@ def attn_fwd_stats(q, k, v, causal=False, scale=None, out=None, m_out=None, l_ou
             m_out = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
         if l_out is None:
             l_out = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
-    with torch.cuda.device(q.device):
-        sh = _stream_handle(stream, q.device)
+    with _on_device(q):
+        sh = _stream_handle(stream, q.get_device())
         args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                 ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
                 b, h, nq, nk, d, int(bool(causal)), float(scale), _DTYPES[q.dtype])
@@ -168,8 +200,8 @@ def attn_bwd(q, k, v, out, dout, m, l, causal=False, scale=None, dq=None, dk=Non
         if (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device
                 or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous tensor like {'q' if like is q else 'k'}")
-    with torch.cuda.device(q.device):
-        sh = _stream_handle(stream, q.device)
+    with _on_device(q):
+        sh = _stream_handle(stream, q.get_device())
         ptrs = (ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out, dout, m, l, dq, dk, dv))
         rc = lib().attn_bwd(*ptrs, b, h, hkv, nq, nk, d, int(bool(causal)), float(scale),
                             _DTYPES[q.dtype], sh)
@@ -221,15 +253,15 @@ def attn_fwd_masked(q, k, v, mask=None, causal=False, window=0, scale=None, out=
         scale = default_scale(d)
     if out is None:
         out = torch.empty_like(q)
-    elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
-          or not out.is_contiguous()):
+    elif (out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda
+          or out.get_device() != q.get_device() or not out.is_contiguous()):
         raise ValueError("out must be a contiguous tensor like q")
     m = l = None
     if want_stats:
         m = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
         l = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
-    with torch.cuda.device(q.device):
-        sth = _stream_handle(stream, q.device)
+    with _on_device(q):
+        sth = _stream_handle(stream, q.get_device())
         rc = lib().attn_fwd_masked(
             *(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out)),
             ctypes.c_void_p(mask.data_ptr()) if mask is not None else None, sb, sh,
@@ -253,15 +285,15 @@ def attn_fwd_dropout(q, k, v, p, seed, offset=0, causal=False, scale=None, out=N
         scale = default_scale(d)
     if out is None:
         out = torch.empty_like(q)
-    elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
-          or not out.is_contiguous()):
+    elif (out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda
+          or out.get_device() != q.get_device() or not out.is_contiguous()):
         raise ValueError("out must be a contiguous tensor like q")
     m = l = None
     if want_stats:
         m = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
         l = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
-    with torch.cuda.device(q.device):
-        sth = _stream_handle(stream, q.device)
+    with _on_device(q):
+        sth = _stream_handle(stream, q.get_device())
         rc = lib().attn_fwd_dropout(
             *(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out)), b, h, hkv, nq, nk, d,
             int(bool(causal)), float(scale), float(p), int(seed), int(offset), _DTYPES[q.dtype],
@@ -304,15 +336,15 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, caus
         scale = default_scale(d)
     if out is None:
         out = torch.empty_like(q)
-    elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
-          or not out.is_contiguous()):
+    elif (out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda
+          or out.get_device() != q.get_device() or not out.is_contiguous()):
         raise ValueError("out must be a contiguous tensor like q")
     m = l = None
     if want_stats:
         m = torch.empty((h, total_q), dtype=torch.float32, device=q.device)
         l = torch.empty((h, total_q), dtype=torch.float32, device=q.device)
-    with torch.cuda.device(q.device):
-        sh = _stream_handle(stream, q.device)
+    with _on_device(q):
+        sh = _stream_handle(stream, q.get_device())
         stats = ((ctypes.c_void_p(m.data_ptr()), ctypes.c_void_p(l.data_ptr()))
                  if want_stats else (None, None))
         rc = lib().attn_fwd_varlen(
@@ -369,8 +401,8 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, causal=True, w
         scale = default_scale(d)
     if out is None:
         out = torch.empty_like(q)
-    elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
-          or not out.is_contiguous()):
+    elif (out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda
+          or out.get_device() != q.get_device() or not out.is_contiguous()):
         raise ValueError("out must be a contiguous tensor like q")
     if want_stats:
         m_out = torch.empty((b, h, nq), dtype=torch.float32, device=q.device) if m_out is None else m_out
@@ -379,8 +411,8 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, causal=True, w
             if (t.dtype != torch.float32 or t.device != q.device or t.shape != (b, h, nq)
                     or not t.is_contiguous()):
                 raise ValueError(f"{name} must be a contiguous float32 [B, H, Nq] GPU tensor")
-    with torch.cuda.device(q.device):
-        sh = _stream_handle(stream, q.device)
+    with _on_device(q):
+        sh = _stream_handle(stream, q.get_device())
         stats = ((ctypes.c_void_p(m_out.data_ptr()), ctypes.c_void_p(l_out.data_ptr()))
                  if want_stats else (None, None))
         rc = getattr(lib(), _entry)(
@@ -422,8 +454,8 @@ def online_merge_batch(m1, l1, m2, l2, m=None, l=None, stream=None):
     for t in (m, l):
         if t.shape != m1.shape or t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError("outputs must be contiguous float32 tensors like the inputs")
-    with torch.cuda.device(m1.device):
-        sh = _stream_handle(stream, m1.device)
+    with _on_device(m1):
+        sh = _stream_handle(stream, m1.get_device())
         rc = lib().online_merge_batch(*(ctypes.c_void_p(t.data_ptr()) for t in (*ts, m, l)),
                                       m1.numel(), sh)
     _check(rc, "online_merge_batch")
@@ -448,8 +480,8 @@ def softmax_rows(x, chunk=0, out=None, stream=None):
     elif (out.shape != x.shape or out.dtype != x.dtype or out.device != x.device
           or not out.is_contiguous()):
         raise ValueError("out must be a contiguous tensor like x")
-    with torch.cuda.device(x.device):
-        sh = _stream_handle(stream, x.device)
+    with _on_device(x):
+        sh = _stream_handle(stream, x.get_device())
         rc = lib().softmax_rows(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
                                 x.shape[0], x.shape[1], int(chunk), _DTYPES[x.dtype], sh)
     _check(rc, "softmax_rows")

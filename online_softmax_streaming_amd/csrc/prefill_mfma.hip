@@ -524,9 +524,11 @@ void prefill_mfma_kernel(PrefillArgs a) {
         need_cur = any_need(t_first & 1);
         need_next = any_need((t_first + 1) & 1);
       }
-      // Key tile of step t (plain batched causal layout, second pass: from
-      // the diagonal down; every other case in increasing order).
-      const bool down = MODE == kModeBatched && CAUSAL && pass == 1;
+      // Key tile of step t: the second causal pass runs from the diagonal
+      // down (plain, packed and dropout layouts alike, so they agree bit for
+      // bit); the masked layout, whose tile votes look two tiles ahead, and
+      // every first pass run in increasing order.
+      const bool down = !MASKED && CAUSAL && pass == 1;
       auto tile_of = [&](int t) __attribute__((always_inline)) { return down ? ntiles - 1 - t : t; };
       if (need_cur) load_tile(tile_of(t_first) * BN, 0);
       __syncthreads();

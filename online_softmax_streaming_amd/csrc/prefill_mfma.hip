@@ -136,8 +136,10 @@ void prefill_mfma_kernel(PrefillArgs a) {
   // direct-to-LDS loads into one from the operand reads of the other.
   __shared__ __attribute__((aligned(1024))) unsigned char smem0[2][TILE];  // [K, V]
   __shared__ __attribute__((aligned(1024))) unsigned char smem1[2][TILE];
-  // Per-wave votes on whether a future key tile is needed (masked mode).
-  __shared__ int tile_need[2][NW];
+  // Under a mask: which key tiles hold a key visible to some row of the
+  // workgroup's query tile (bit b covers tiles t_first + b*g .. + g-1).
+  constexpr int kTileBitWords = MASKED ? 256 : 1;
+  __shared__ uint32_t tile_bits[kTileBitWords];
   auto tile_ptr = [&](int buf, int kv) __attribute__((always_inline)) -> unsigned char* {
     return buf == 0 ? &smem0[kv][0] : &smem1[kv][0];
   };
@@ -492,89 +494,155 @@ void prefill_mfma_kernel(PrefillArgs a) {
         if (MASKED && win > 0) act = act && ju + BN - 1 > qw0 + off - win;
         return act;
       };
-      // Under a mask, tiles no row of the workgroup may see are neither
-      // staged nor computed: each wave votes on tile t+2 during step t (its
-      // rows' mask words are fetched two tiles ahead), the votes meet in LDS
-      // across the step's barrier, and step t+1 stages tile t+2 only if some
-      // wave needs it.  Flags of tile u live in tile_need[u & 1]; they are
-      // written in step u-2 and read right after that step's barrier, and
-      // the next write to the same slot comes two barriers later.
+      // Under a mask, key tiles no row of the workgroup may see are neither
+      // staged nor computed, and cost no step: before the key loop the
+      // workgroup maps which tiles of [t_first, ntiles) hold a visible key
+      // for some row (its rows' mask words, clipped to each row's causal and
+      // window range), and the loop walks only those.  Bit b covers g tiles
+      // (g = 1 unless more than 8192 tiles are in range).
       const bool skip_tiles = MASKED && a.mask != nullptr;
-      auto any_need = [&](int slot) __attribute__((always_inline)) {
-        int v = 0;
-  #pragma unroll
-        for (int w = 0; w < NW; ++w) v |= tile_need[slot][w];
-        return __builtin_amdgcn_readfirstlane(v) != 0;
-      };
-      // Mask words of this lane's row: tile t (mw), t+1 (nw), t+2 (xw).
-      uint32_t nw0 = mask_word(2 * t_first), nw1 = mask_word(2 * t_first + 1);
-      uint32_t xw0 = 0, xw1 = 0;
-      bool need_cur = true, need_next = true;
+      constexpr int kTileBits = 32 * kTileBitWords;
+      const int span = ntiles - t_first;
+      const int g = skip_tiles ? (span + kTileBits - 1) / kTileBits : 1;
       if (skip_tiles) {
-        xw0 = mask_word(2 * t_first + 2);
-        xw1 = mask_word(2 * t_first + 3);
-        const bool n0 = wave_active(t_first) && __builtin_amdgcn_ballot_w64((nw0 | nw1) != 0u) != 0;
-        const bool n1 = t_first + 1 < ntiles && wave_active(t_first + 1) &&
-                        __builtin_amdgcn_ballot_w64((xw0 | xw1) != 0u) != 0;
-        if (lane == 0) {
-          tile_need[t_first & 1][wave] = n0;
-          tile_need[(t_first + 1) & 1][wave] = n1;
-        }
+        for (int w = tid; w < kTileBitWords; w += NT) tile_bits[w] = 0u;
         __syncthreads();
-        need_cur = any_need(t_first & 1);
-        need_next = any_need((t_first + 1) & 1);
-      }
-      // Key tile of step t: the second causal pass runs from the diagonal
-      // down (plain, packed and dropout layouts alike, so they agree bit for
-      // bit); the masked layout, whose tile votes look two tiles ahead, and
-      // every first pass run in increasing order.
-      const bool down = !MASKED && CAUSAL && pass == 1;
-      auto tile_of = [&](int t) __attribute__((always_inline)) { return down ? ntiles - 1 - t : t; };
-      if (need_cur) load_tile(tile_of(t_first) * BN, 0);
-      __syncthreads();
-      auto step = [&](auto bufc, int t) {
-        constexpr int buf = decltype(bufc)::value;
-        const int j0 = tile_of(t) * BN;
-        const bool more = t + 1 < ntiles;
-        if (more && need_next) load_tile(tile_of(t + 1) * BN, buf ^ 1);  // in flight while this tile is computed
-        const uint32_t mw0 = nw0, mw1 = nw1;
-        uint32_t fw0 = 0, fw1 = 0;  // words of tile t+2 (tile skipping only)
-        if (MASKED && more) {
-          if (skip_tiles) {
-            nw0 = xw0;
-            nw1 = xw1;
-            fw0 = mask_word(j0 / 32 + 4);
-            fw1 = mask_word(j0 / 32 + 5);
-          } else {
-            nw0 = mask_word(j0 / 32 + 2);
-            nw1 = mask_word(j0 / 32 + 3);
+        // Two threads per row, alternate mask words; loads go out in
+        // batches so their latencies overlap.
+        const int r = tid >> 1, par = tid & 1;
+        const int i = i0 + r;
+        if (r < BM && i >= 0 && i < Nq) {
+          const int b = bh / a.H, h = bh - b * a.H;
+          const uint32_t* row = a.mask + (int64_t)b * a.mask_sb + (int64_t)h * a.mask_sh +
+                                (int64_t)i * a.mask_words;
+          // Keys this row may see at all: [klo, khi).
+          int khi = Nk;
+          if (CAUSAL) khi = min(khi, i + off + 1);
+          khi = min(khi, ntiles * BN);
+          int klo = t_first * BN;
+          if (win > 0) klo = max(klo, i + off - win + 1);
+          if (khi > klo) {
+            const int wlo = klo >> 5, whi = (khi + 31) >> 5;
+            // Sets the bit of each tile whose (clipped) words in x[] are not
+            // all zero; x[e] is word w0 + e * step.
+            auto mark = [&](const uint32_t* x, int n, int w0, int wstep) __attribute__((always_inline)) {
+              uint32_t bits = 0u;
+              int bw = -1;  // bitmap word `bits` belongs to
+              for (int e = 0; e < n; ++e) {
+                const int w = w0 + e * wstep;
+                uint32_t xv = w >= wlo && w < whi ? x[e] : 0u;
+                if (w == (klo >> 5)) xv &= ~0u << (klo & 31);
+                if (w == ((khi - 1) >> 5) && (khi & 31)) xv &= ~0u >> (32 - (khi & 31));
+                if (xv != 0u) {
+                  const int bb = ((w >> 1) - t_first) / g;
+                  if ((bb >> 5) != bw) {
+                    if (bits) atomicOr(&tile_bits[bw], bits);
+                    bw = bb >> 5;
+                    bits = 0u;
+                  }
+                  bits |= 1u << (bb & 31);
+                }
+              }
+              if (bits) atomicOr(&tile_bits[bw], bits);
+            };
+            if ((a.mask_words & 3) == 0 && (reinterpret_cast<uintptr_t>(row) & 15) == 0) {
+              // 16-byte loads (rows of whole 4-word chunks, so no chunk runs
+              // past its row): the pair's threads take alternate chunks, 8
+              // in flight per thread.
+              constexpr int kBatch = 8;
+              for (int c0 = (wlo >> 2) + par; 4 * c0 < whi; c0 += 2 * kBatch) {
+                uint32_t x[4 * kBatch];
+  #pragma unroll
+                for (int e = 0; e < kBatch; ++e) {
+                  const int c = c0 + 2 * e;
+                  const u32x4 v = 4 * c < whi ? *reinterpret_cast<const u32x4*>(row + 4 * c) : u32x4{};
+  #pragma unroll
+                  for (int f = 0; f < 4; ++f) x[4 * e + f] = v[f];
+                }
+  #pragma unroll
+                for (int e = 0; e < kBatch; ++e) mark(x + 4 * e, 4, 4 * (c0 + 2 * e), 1);
+              }
+            } else {
+              // Word loads: alternate words, 16 in flight per thread.
+              constexpr int kBatch = 16;
+              for (int w0 = wlo + par; w0 < whi; w0 += 2 * kBatch) {
+                uint32_t x[kBatch];
+  #pragma unroll
+                for (int e = 0; e < kBatch; ++e) {
+                  const int w = w0 + 2 * e;
+                  x[e] = w < whi ? row[w] : 0u;
+                }
+                mark(x, kBatch, w0, 2);
+              }
+            }
           }
         }
-        bool active = need_cur && wave_active(tile_of(t));
+        __syncthreads();
+      }
+      // The next key tile after t the workgroup needs (ntiles if none).
+      auto next_tile = [&](int t) __attribute__((always_inline)) -> int {
+        if (!skip_tiles) return t + 1;
+        int u = t + 1;
+        if (u >= ntiles) return ntiles;
+        int b = (u - t_first) / g;
+        if ((u - t_first) % g != 0) return u;  // inside the super tile being walked
+        const int nbits = (span + g - 1) / g;
+        while (b < nbits) {
+          const uint32_t word =
+              __builtin_amdgcn_readfirstlane(tile_bits[b >> 5]) & (~0u << (b & 31));
+          if (word != 0u) return min(ntiles, t_first + (32 * (b >> 5) + __builtin_ctz(word)) * g);
+          b = 32 * ((b >> 5) + 1);
+        }
+        return ntiles;
+      };
+      // Key tile of step t: the second causal pass runs from the diagonal
+      // down (plain, packed and dropout layouts alike, so they agree bit for
+      // bit); the masked layout and every first pass run in increasing order.
+      const bool down = !MASKED && CAUSAL && pass == 1;
+      auto tile_of = [&](int t) __attribute__((always_inline)) { return down ? ntiles - 1 - t : t; };
+      const int t_start = skip_tiles ? next_tile(t_first - 1) : t_first;
+      // Mask words of this lane's row for the tile being computed (mw) and
+      // the next one (nw), fetched one step ahead.
+      uint32_t nw0 = 0u, nw1 = 0u;
+      if (MASKED && t_start < ntiles) {
+        nw0 = mask_word(2 * t_start);
+        nw1 = mask_word(2 * t_start + 1);
+      }
+      if (t_start < ntiles) load_tile(tile_of(t_start) * BN, 0);
+      __syncthreads();
+      auto step = [&](auto bufc, int t, int tn) {
+        constexpr int buf = decltype(bufc)::value;
+        const int j0 = tile_of(t) * BN;
+        if (tn < ntiles) load_tile(tile_of(tn) * BN, buf ^ 1);  // in flight while this tile is computed
+        const uint32_t mw0 = nw0, mw1 = nw1;
+        if (MASKED && tn < ntiles) {
+          nw0 = mask_word(2 * tn);
+          nw1 = mask_word(2 * tn + 1);
+        }
+        bool active = wave_active(tile_of(t));
         // A tile none of this wave's rows may see under the mask is skipped.
         if (MASKED && a.mask) active = active && __builtin_amdgcn_ballot_w64((mw0 | mw1) != 0u) != 0;
         if (active) {
           bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > qw0 + off);
-          if (MASKED) need_mask = need_mask || a.mask || (win > 0 && j0 <= q_last + off - win);
+          // Mask bits are applied only where some row of the wave hides a
+          // key of the tile (a tile wholly inside every row's mask costs no
+          // mask work).
+          if (MASKED)
+            need_mask = need_mask || (win > 0 && j0 <= q_last + off - win) ||
+                        (a.mask && __builtin_amdgcn_ballot_w64((mw0 & mw1) != ~0u) != 0);
           compute(bufc, j0, need_mask, mw0, mw1);
         }
-        if (skip_tiles) {
-          const bool n2 = t + 2 < ntiles && wave_active(t + 2) &&
-                          __builtin_amdgcn_ballot_w64((fw0 | fw1) != 0u) != 0;
-          if (lane == 0) tile_need[t & 1][wave] = n2;  // slot of tile t+2
-          xw0 = fw0;
-          xw1 = fw1;
-        }
-        // Buffer buf^1 was last read in step t-1, before that step's barrier.
+        // Buffer buf^1 was last read in the previous step, before its barrier.
         __syncthreads();
-        if (skip_tiles) {
-          need_cur = need_next;
-          need_next = any_need(t & 1);
-        }
       };
-      for (int t = t_first; t < ntiles; t += 2) {
-        step(std::integral_constant<int, 0>{}, t);
-        if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
+      for (int t = t_start; t < ntiles;) {
+        int tn = next_tile(t);
+        step(std::integral_constant<int, 0>{}, t, tn);
+        t = tn;
+        if (t >= ntiles) break;
+        tn = next_tile(t);
+        step(std::integral_constant<int, 1>{}, t, tn);
+        t = tn;
       }
     }
 

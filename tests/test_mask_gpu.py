@@ -75,6 +75,60 @@ def test_parity_random_mask(lib, dtype, causal, b, h, hkv, nq, nk, d, density):
     _check(lib, q, k, v, mask, causal, 0, dtype)
 
 
+def _doc_mask(nq, nk, doc):
+    i = torch.arange(nq)[:, None] + (nk - nq)
+    j = torch.arange(nk)[None, :]
+    return ((i // doc) == (j // doc))[None, None].cuda()
+
+
+def _block_mask(nq, nk, seed, p_block=0.3, density=0.6):
+    # Whole (64-row, 64-key) blocks switched on with probability p_block,
+    # random bits inside them: query tiles then need scattered key tiles
+    # with empty ones between them.
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    blocks = torch.rand(((nq + 63) // 64, (nk + 63) // 64), generator=g) < p_block
+    full = blocks.repeat_interleave(64, 0).repeat_interleave(64, 1)[:nq, :nk]
+    bits = torch.rand((nq, nk), generator=g) < density
+    return (full & bits)[None, None].cuda()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk,doc", [(1024, 1024, 200), (900, 900, 96), (640, 1280, 512)])
+def test_document_masks(lib, dtype, causal, nq, nk, doc):
+    # Block-diagonal masks: each query tile needs a few key tiles, the rest
+    # are skipped by the workgroup's tile map.  Key counts with whole 4-word
+    # mask chunks per row (1024, 1280) and without (900) take the two load
+    # paths of the map.
+    q, k, v = _inputs(2, 2, 1, nq, nk, 64, dtype, seed=nq + doc)
+    _check(lib, q, k, v, _doc_mask(nq, nk, doc), causal, 0, dtype)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(700, 1500), (513, 2049)])
+def test_block_sparse_masks(lib, causal, nq, nk):
+    q, k, v = _inputs(1, 2, 2, nq, nk, 128, "bf16", seed=nq)
+    _check(lib, q, k, v, _block_mask(nq, nk, seed=nk), causal, 0, "bf16")
+
+
+def test_block_sparse_mask_with_window(lib):
+    q, k, v = _inputs(1, 2, 1, 800, 1200, 64, "f16", seed=11)
+    _check(lib, q, k, v, _block_mask(800, 1200, seed=12, p_block=0.5), True, 300, "f16")
+
+
+def test_tile_map_coarse_over_many_keys(lib):
+    # 540,000 keys = 8438 key tiles: more than the map's 8192 bits, so each
+    # bit covers two tiles.  Block-sparse mask, 40 rows.
+    nq, nk = 40, 540000
+    q, k, v = _inputs(1, 1, 1, nq, nk, 64, "bf16", seed=13)
+    g = torch.Generator(device="cpu").manual_seed(14)
+    on = torch.rand(((nk + 4095) // 4096,), generator=g) < 0.2
+    full = on.repeat_interleave(4096)[:nk][None, :].expand(nq, nk)
+    bits = torch.rand((nq, nk), generator=g) < 0.5
+    mask = (full & bits)[None, None].cuda()
+    _check(lib, q, k, v, mask, False, 0, "bf16")
+
+
 @pytest.mark.parametrize("bm,hm", [(1, 1), (2, 1), (1, 4)])
 def test_broadcast_masks(lib, bm, hm):
     q, k, v = _inputs(2, 4, 2, 200, 300, 64, "bf16", seed=bm * 10 + hm)

@@ -140,6 +140,11 @@ void prefill_mfma_kernel(PrefillArgs a) {
   // workgroup's query tile (bit b covers tiles t_first + b*g .. + g-1).
   constexpr int kTileBitWords = MASKED ? 256 : 1;
   __shared__ uint32_t tile_bits[kTileBitWords];
+  // Packed sequences: key counts of up to kSortMaxB sequences, and the
+  // sequence a workgroup takes (see below).
+  constexpr int kSortMaxB = VARLEN ? 1024 : 1;
+  __shared__ int seq_keys[kSortMaxB];
+  __shared__ int seq_pick;
   auto tile_ptr = [&](int buf, int kv) __attribute__((always_inline)) -> unsigned char* {
     return buf == 0 ? &smem0[kv][0] : &smem1[kv][0];
   };
@@ -173,8 +178,31 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // Head-major order: each XCD's contiguous range of workgroups then holds
     // a few heads of every sequence, so ragged sequence lengths do not pile
     // the long sequences onto some XCDs (batch-major order would give each
-    // XCD a few whole sequences).
-    const int h = bh / a.B, b = bh - h * a.B;
+    // XCD a few whole sequences).  Within a head the sequences go in
+    // decreasing key count (ties by index), so the longest workgroups start
+    // first and the short ones fill in behind them (up to kSortMaxB
+    // sequences; beyond that, input order).
+    const int h = bh / a.B;
+    int b = bh - h * a.B;
+    if (a.B > 1 && a.B <= kSortMaxB) {
+      const int kq = b;
+      for (int s = threadIdx.x; s < a.B; s += NW * 64) {
+        const int s0 = min(max(a.cu_k[s], 0), a.total_k);
+        seq_keys[s] = min(max(a.cu_k[s + 1], s0), a.total_k) - s0;
+      }
+      __syncthreads();
+      for (int s = threadIdx.x; s < a.B; s += NW * 64) {
+        const int ks = seq_keys[s];
+        int rank = 0;
+        for (int s2 = 0; s2 < a.B; ++s2) {
+          const int k2 = seq_keys[s2];
+          rank += k2 > ks || (k2 == ks && s2 < s);
+        }
+        if (rank == kq) seq_pick = s;
+      }
+      __syncthreads();
+      b = seq_pick;
+    }
     const int q0 = min(max(a.cu_q[b], 0), a.total_q);
     const int q1 = min(max(a.cu_q[b + 1], q0), a.total_q);
     const int k0 = min(max(a.cu_k[b], 0), a.total_k);

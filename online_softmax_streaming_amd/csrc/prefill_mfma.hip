@@ -552,7 +552,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
           if (khi > klo) {
             const int wlo = klo >> 5, whi = (khi + 31) >> 5;
             // Sets the bit of each tile whose (clipped) words in x[] are not
-            // all zero; x[e] is word w0 + e * step.
+            // all zero; x[e] is word w0 + e * wstep.
             auto mark = [&](const uint32_t* x, int n, int w0, int wstep) __attribute__((always_inline)) {
               uint32_t bits = 0u;
               int bw = -1;  // bitmap word `bits` belongs to

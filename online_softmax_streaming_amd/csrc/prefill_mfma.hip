@@ -141,8 +141,10 @@ void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int kTileBitWords = MASKED ? 256 : 1;
   __shared__ uint32_t tile_bits[kTileBitWords];
   // Packed sequences: key counts of up to kSortMaxB sequences, and the
-  // sequence a workgroup takes (see below).
-  constexpr int kSortMaxB = VARLEN ? 1024 : 1;
+  // sequence a workgroup takes (see below).  The ranking costs each
+  // workgroup about B*B/(64*NW) LDS reads, so it stops at 64 sequences; with
+  // many sequences the hardware's dispatch already interleaves their lengths.
+  constexpr int kSortMaxB = VARLEN ? 64 : 1;
   __shared__ int seq_keys[kSortMaxB];
   __shared__ int seq_pick;
   auto tile_ptr = [&](int buf, int kv) __attribute__((always_inline)) -> unsigned char* {
@@ -180,7 +182,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // the long sequences onto some XCDs (batch-major order would give each
     // XCD a few whole sequences).  Within a head the sequences go in
     // decreasing key count (ties by index), so the longest workgroups start
-    // first and the short ones fill in behind them (up to kSortMaxB
+    // first and the short ones fill in behind them (up to kSortMaxB = 64
     // sequences; beyond that, input order).
     const int h = bh / a.B;
     int b = bh - h * a.B;

@@ -63,6 +63,18 @@ def test_parity(lib, dtype, causal, h, hkv, d, lens_q, lens_k):
     _check(lib, inputs, causal, dtype)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nseq", [40, 90])
+def test_many_sequences_of_mixed_lengths(lib, causal, nseq):
+    # 40 sequences: workgroups take them in decreasing key count (ranked in
+    # LDS, ties included); 90: beyond the ranking's 64, input order.
+    g = np.random.default_rng(nseq)
+    lens = [int(x) for x in g.integers(1, 700, size=nseq)]
+    lens[3] = lens[7] = lens[11] = 333  # ties in the ranking
+    inputs = make_varlen(lens, lens, 4, 2, 64, "bf16", seed=nseq, device="cuda")
+    _check(lib, inputs, causal, "bf16")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_equal_lengths_equal_batched_kernel(lib, dtype, causal):

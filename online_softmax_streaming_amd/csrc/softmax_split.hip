@@ -86,22 +86,28 @@ __device__ __forceinline__ State chunk_state(const T* __restrict__ xr, int64_t e
   constexpr int VEC = SmVec<T>::n;
   State s{kNegInf, 0.f};
   if (vec) {
-    for (int64_t e = e0 + (int64_t)threadIdx.x * VEC; e < e1; e += (int64_t)kSmThreads * VEC) {
-      const vt v = *reinterpret_cast<const vt*>(xr + e);
-      float f[VEC];
+    // Two vectors per step (both loads in flight), one maximum over their
+    // 2*VEC elements, then one exponential per element against it.
+    constexpr int64_t STEP = (int64_t)kSmThreads * VEC;
+    for (int64_t e = e0 + (int64_t)threadIdx.x * VEC; e < e1; e += 2 * STEP) {
+      const bool two = e + STEP < e1;
+      const vt v0 = *reinterpret_cast<const vt*>(xr + e);
+      const vt v1 = two ? *reinterpret_cast<const vt*>(xr + e + STEP) : vt{};
+      float f[2 * VEC];
       float mv = kNegInf;
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
-        f[i] = to_f32<T>(v[i]);
-        mv = fmaxf(mv, f[i]);
+        f[i] = to_f32<T>(v0[i]);
+        f[VEC + i] = two ? to_f32<T>(v1[i]) : kNegInf;
+        mv = fmaxf(mv, fmaxf(f[i], f[VEC + i]));
       }
-      // A vector of masked (-inf) entries is the empty state (-inf, 0): its
+      // A run of masked (-inf) entries is the empty state (-inf, 0): its
       // exponents are taken against the pinned reference 0, never
       // (-inf) - (-inf).
       const float rv = pinned_ref(mv);
       float lv = 0.f;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) lv += exp2_hw((f[i] - rv) * kLog2e);
+      for (int i = 0; i < 2 * VEC; ++i) lv += exp2_hw((f[i] - rv) * kLog2e);
       s = merge(s, State{mv, lv});
     }
   } else {

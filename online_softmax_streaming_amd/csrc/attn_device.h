@@ -48,6 +48,31 @@ __device__ __forceinline__ MergeWeights merge_weights_log2(float m1, float m2) {
   return r;
 }
 
+// The full 128-bit product a * m as (lo, hi), from four 32 x 32 -> 64
+// products: with a = a1 2^32 + a0 and m = m1 2^32 + m0, t = a1 m0 + hi(a0 m0)
+// and u = a0 m1 + lo(t) cannot overflow 64 bits, lo = lo(u) 2^32 + lo(a0 m0)
+// and hi = a1 m1 + hi(t) + hi(u).  Each product is one 32-bit multiply-add
+// into a 64-bit register pair, where hi and lo taken separately would redo
+// the cross products.
+__device__ __forceinline__ void mul_wide(uint64_t a, uint64_t m, uint64_t& lo, uint64_t& hi) {
+  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32), m0 = (uint32_t)m, m1 = (uint32_t)(m >> 32);
+  const uint64_t p00 = (uint64_t)a0 * m0;
+  const uint64_t t = (uint64_t)a1 * m0 + (p00 >> 32);
+  const uint64_t u = (uint64_t)a0 * m1 + (uint32_t)t;
+  hi = (uint64_t)a1 * m1 + (t >> 32) + (u >> 32);
+  lo = (u << 32) | (uint32_t)p00;
+}
+
+// a ^ b ^ c with one three-input bitwise operation per 32-bit half (truth
+// table 0x96: odd parity of the three bits); the compiler otherwise issues
+// two two-input xors.
+__device__ __forceinline__ uint64_t xor3(uint64_t a, uint64_t b, uint64_t c) {
+  const uint32_t lo = __builtin_amdgcn_bitop3_b32((uint32_t)a, (uint32_t)b, (uint32_t)c, 0x96);
+  const uint32_t hi = __builtin_amdgcn_bitop3_b32((uint32_t)(a >> 32), (uint32_t)(b >> 32),
+                                                  (uint32_t)(c >> 32), 0x96);
+  return (uint64_t)lo | ((uint64_t)hi << 32);
+}
+
 // Philox4x64-10, the counter-based generator of Salmon, Moraes, Dror and
 // Shaw ("Parallel random numbers: as easy as 1, 2, 3", SC 2011): ten rounds
 // on a 4-word counter under a 2-word key.  Each round multiplies counter
@@ -64,9 +89,10 @@ __device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uin
       k0 += W0;
       k1 += W1;
     }
-    const uint64_t lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
-    const uint64_t lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
-    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    uint64_t lo0, hi0, lo1, hi1;
+    mul_wide(c[0], M0, lo0, hi0);
+    mul_wide(c[2], M1, lo1, hi1);
+    const uint64_t n0 = xor3(hi1, c[1], k0), n2 = xor3(hi0, c[3], k1);
     c[0] = n0;
     c[1] = lo1;
     c[2] = n2;

@@ -460,9 +460,13 @@ void prefill_mfma_kernel(PrefillArgs a) {
       if (DROPOUT) {
         // Group c2 of pf holds keys j0 + 16c2 + t with t = 4*h32 + e%4 +
         // 8*(e/4): fields t of Philox block ((j0 / 16) + c2, qrow, bh,
-        // offset), i.e. words h32 and h32 + 2 of it.  The two lanes of a row
-        // (h32 = 0, 1) each run two of the four blocks (groups 2*h32,
-        // 2*h32 + 1) and swap the two words the other lane needs.
+        // offset), i.e. words h32 and h32 + 2 of it.  The lanes of half h32
+        // run blocks 2*h32 + cc (cc = 0, 1) of their row in full.  A
+        // permlane32 swap of (word 2x, word 2x + 1) trades the upper half's
+        // first register for the lower half's second, which leaves in every
+        // lane word h32 + 2x of block cc in the first register and of block
+        // 2 + cc in the second: the words this lane's groups need, with no
+        // per-lane choice.
         uint64_t own[2][4];
   #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
@@ -472,34 +476,42 @@ void prefill_mfma_kernel(PrefillArgs a) {
           own[cc][3] = a.offset;
           philox4x64_10(own[cc], a.seed, 0);
         }
-        uint64_t recv[2][2];
+        // fw[c2][k]: the two 16-bit fields of 32-bit register k of pf[c2].
+        uint32_t fw[BN / 16][4];
   #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
+        for (int cc = 0; cc < 2; ++cc)
   #pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            const uint64_t send = h32 ? own[cc][2 * x] : own[cc][2 * x + 1];  // word (1-h32) + 2x
-            uint32_t halves[2];
+          for (int x = 0; x < 2; ++x)
   #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-              const uint32_t v32 = (uint32_t)(send >> (32 * hf));
-              const auto r = __builtin_amdgcn_permlane32_swap(v32, v32, false, false);
-              halves[hf] = h32 ? r[0] : r[1];  // the value of lane l ^ 32
+              const auto r = __builtin_amdgcn_permlane32_swap(
+                  (uint32_t)(own[cc][2 * x] >> (32 * hf)),
+                  (uint32_t)(own[cc][2 * x + 1] >> (32 * hf)), false, false);
+              fw[cc][2 * x + hf] = r[0];
+              fw[2 + cc][2 * x + hf] = r[1];
             }
-            recv[cc][x] = (uint64_t)halves[0] | ((uint64_t)halves[1] << 32);
-          }
-        }
-        const vec8 zero8 = vec8{};
+        // Keep a weight iff its field is >= T, two weights per 32-bit
+        // register: d = max(T - field, 0) and g = max(1 - d, 0) per 16-bit
+        // half (saturating packed subtracts), so g = 1 exactly for a kept
+        // weight and 0 otherwise, and the packed 16-bit product of the
+        // weight's bits with g keeps or clears them.  Written out because
+        // the compiler turns the same arithmetic in C into two compares and
+        // two selects per register.
+        const uint32_t t2 = a.drop_t * 0x10001u, one2 = 0x10001u;
   #pragma unroll
         for (int c2 = 0; c2 < BN / 16; ++c2) {
-          const bool mine = (c2 >> 1) == h32;
-          const uint64_t w_lo = mine ? (h32 ? own[c2 & 1][1] : own[c2 & 1][0]) : recv[c2 & 1][0];
-          const uint64_t w_hi = mine ? (h32 ? own[c2 & 1][3] : own[c2 & 1][2]) : recv[c2 & 1][1];
+          uint32_t pw[4];
+          __builtin_memcpy(pw, &pf[c2], sizeof(pw));
   #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint64_t w = e < 4 ? w_lo : w_hi;
-            const uint32_t field = (uint32_t)(w >> (16 * (e & 3))) & 0xFFFFu;
-            pf[c2][e] = field >= a.drop_t ? pf[c2][e] : zero8[e];
+          for (int k = 0; k < 4; ++k) {
+            uint32_t g;
+            asm("v_pk_sub_u16 %1, %2, %3 clamp\n\t"
+                "v_pk_sub_u16 %1, %4, %1 clamp\n\t"
+                "v_pk_mul_lo_u16 %0, %5, %1"
+                : "=v"(pw[k]), "=&v"(g)
+                : "v"(t2), "v"(fw[c2][k]), "v"(one2), "v"(pw[k]));
           }
+          __builtin_memcpy(&pf[c2], pw, sizeof(pw));
         }
       }
 

@@ -7,12 +7,18 @@
 // and contracts"; answer-key page, row A3): S = K Q^T and O += P V on the
 // matrix cores, the online-softmax update with a lazily refreshed reference
 // max, masks only on tiles that cross the diagonal or the ragged end.  Wave
-// w of the KS waves streams key tiles w, w + KS, w + 2 KS, ... of the block,
-// each through its own double-buffered LDS tiles (direct-to-LDS loads, the
-// next tile in flight while one is computed), so the waves never wait on
-// each other until the end.  There the states (m, l, O) are combined with
-// the merge of the answer-key page's row A1: each is rescaled by
-// 2^(m_w - M) to the common reference M = max_w m_w, then summed.
+// w of the KS waves streams key tiles w, w + KS, w + 2 KS, ... of the block
+// through LDS tiles of its own, the next tile in flight while one is
+// computed, so the waves never wait on each other until the end.  There the
+// states (m, l, O) are combined with the merge of the answer-key page's row
+// A1: each is rescaled by 2^(m_w - M) to the common reference M = max_w m_w,
+// then summed.
+//
+// Up to D = 64 a wave double-buffers its K and V tiles in LDS (direct-to-LDS
+// loads).  At D = 128 two such pairs per wave would leave room for only two
+// waves, so a wave keeps one pair in LDS and the next tile in registers,
+// written into the pair after the tile in it has been computed: four waves
+// per workgroup instead of two.
 //
 // With B*H*Nq/32 workgroups of KS waves, a problem of a few heads keeps
 // KS times more waves busy than one wave per row block would, and each
@@ -44,40 +50,51 @@ constexpr int kKPF = 4;              // K fragments read ahead of their MFMA
 constexpr int kVPF = 4;              // V^T operands read ahead of their MFMA
 constexpr float kRefreshGap = 8.0f;  // base-2 units, as in prefill_mfma.hip
 
-// Waves per workgroup: the per-wave double buffers of K and V tiles
-// (2 * 2 * 64 * D * 2 bytes) must fit next to each other in LDS.
+// Waves per workgroup, each with its own K and V tiles (64 * D * 2 bytes
+// each) in LDS: two pairs per wave up to D = 64, one pair and the next tile
+// in registers at D = 128.
+constexpr int kSplits = 4;
 template <int D>
-constexpr int kSplits = D > 64 ? 2 : 4;
+constexpr bool kRegStage = D > 64;
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kSplits<D> * 64) void prefill_splitk_kernel(SplitArgs a) {
+__global__ __launch_bounds__(kSplits * 64) void prefill_splitk_kernel(SplitArgs a) {
   typedef typename Mfma<T>::vec8 vec8;
   typedef typename Mfma<T>::vec4 vec4;
   typedef typename Mfma<T>::vec2 vec2;
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   typedef Geo<D> G;
-  constexpr int KS = kSplits<D>;
+  constexpr int KS = kSplits;
+  constexpr bool STAGE = kRegStage<D>;
   constexpr int BN = kBN;
   constexpr int DP = D < 32 ? 32 : D;  // O^T rows, padded to one MFMA block
   constexpr int KC = D / 16;           // k-chunks of Q.K^T
   constexpr int NB = DP / 32;          // 32-row blocks of O^T
   constexpr int TILE = BN * D * 2;     // bytes of one K or V tile
   constexpr int NSLOT = TILE / 16;     // 16-byte slots per tile
+  constexpr int NU = NSLOT / 64;       // 1 KB LDS blocks per tile
   constexpr int NREG = 16 * NB;        // O^T registers per lane
   static_assert(G::steps_keep_swizzle(), "tile steps must keep the LDS swizzle");
   static_assert(NSLOT % 64 == 0, "a wave moves whole 1 KB LDS blocks");
 
   // Buffer parity 0 and 1 as separate objects, so the compiler can tell a
-  // tile being loaded from the one being read; [wave][K or V].
-  __shared__ __attribute__((aligned(1024))) unsigned char buf0[KS][2][TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char buf1[KS][2][TILE];
-  // States of waves 1..KS-1 for the merge: [wave - 1][register][lane].
-  __shared__ float mrg[KS - 1][NREG + 3][64];
+  // tile being loaded from the one being read; [wave][K or V] tiles.  The
+  // states of waves 1..KS-1 for the merge, [wave - 1][register][lane], have
+  // their own array, or (register staging, one pair per wave) take buf0's
+  // place once every tile has been read.
+  constexpr int kPairs = KS * 2 * TILE;
+  constexpr int kMergeFloats = (KS - 1) * (NREG + 3) * 64;
+  constexpr int kBuf0 = STAGE && kMergeFloats * 4 > kPairs ? kMergeFloats * 4 : kPairs;
+  __shared__ __attribute__((aligned(1024))) unsigned char buf0[kBuf0];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf1[STAGE ? 16 : kPairs];
+  __shared__ float mrg_own[STAGE ? 1 : kMergeFloats];
+  float* const mrg = STAGE ? reinterpret_cast<float*>(buf0) : mrg_own;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   auto tile_ptr = [&](int buf, int kv) __attribute__((always_inline)) -> unsigned char* {
-    return buf == 0 ? &buf0[wave][kv][0] : &buf1[wave][kv][0];
+    return buf == 0 ? &buf0[(wave * 2 + kv) * TILE] : &buf1[(wave * 2 + kv) * TILE];
   };
 
   const int bh = blockIdx.x / a.nrb;
@@ -141,22 +158,44 @@ __global__ __launch_bounds__(kSplits<D> * 64) void prefill_splitk_kernel(SplitAr
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
 
-  // Tile t of this wave into buffer buf: lane l moves slots l, l + 64, ...
-  // (slot s holds chunk (s % CPR) ^ swz(row) of row s / CPR); rows past Nk
-  // are out of the buffer range and arrive as zeros.
+  // Slot s of a tile (lane l of 1 KB block u holds slot l + 64u) is chunk
+  // (s % CPR) ^ swz(row) of row s / CPR; rows past Nk are out of the buffer
+  // range and arrive as zeros.
+  auto slot_off = [&](int t, int u) __attribute__((always_inline)) {
+    const int sl = lane + u * 64;
+    const int row = sl / G::CPR;
+    const int chunk = (sl % G::CPR) ^ G::swz(row);
+    const int j = min(t * BN + row, Nk);
+    return (int)((uint32_t)j * kpitch + (uint32_t)(chunk << 4));
+  };
+  // Tile t straight into buffer buf.
   auto load_tile = [&](int t, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
 #pragma unroll
-    for (int u = 0; u < NSLOT / 64; ++u) {
-      const int sl = lane + u * 64;
-      const int row = sl / G::CPR;
-      const int chunk = (sl % G::CPR) ^ G::swz(row);
-      const int j = min(t * BN + row, Nk);
-      const int vo = (int)((uint32_t)j * kpitch + (uint32_t)(chunk << 4));
+    for (int u = 0; u < NU; ++u) {
+      const int vo = slot_off(t, u);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, LDS_PTR(void, tile_ptr(buf, 0) + u * 1024), 16,
                                                vo, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, LDS_PTR(void, tile_ptr(buf, 1) + u * 1024), 16,
                                                vo, 0, 0, 0);
+    }
+  };
+  // Register staging: tile t into registers, and from there into buffer 0
+  // in the same layout.
+  u32x4 kst[STAGE ? NU : 1], vst[STAGE ? NU : 1];
+  auto stage_tile = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int vo = slot_off(t, u);
+      kst[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, vo, 0, 0);
+      vst[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, vo, 0, 0);
+    }
+  };
+  auto unstage_tile = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      *reinterpret_cast<u32x4*>(tile_ptr(0, 0) + u * 1024 + lane * 16) = kst[u];
+      *reinterpret_cast<u32x4*>(tile_ptr(0, 1) + u * 1024 + lane * 16) = vst[u];
     }
   };
 
@@ -251,22 +290,38 @@ __global__ __launch_bounds__(kSplits<D> * 64) void prefill_splitk_kernel(SplitAr
   };
 
   // This wave's tiles: wave, wave + KS, ...; the next one is in flight while
-  // the current one is computed.  Reads of a buffer finish (their values feed
-  // the products) before the same wave reloads it two tiles later.
-  // Each step ends by waiting for its own loads (vmcnt 0), so a step's reads
-  // never wait on the tile it just put in flight.
+  // the current one is computed.
   constexpr int kWaitLoads = 0x0F70;  // s_waitcnt vmcnt(0) (expcnt, lgkmcnt untouched)
   if (qw0 < Nq && wave < ntiles) {
     load_tile(wave, std::integral_constant<int, 0>{});
-    __builtin_amdgcn_s_waitcnt(kWaitLoads);
-    for (int t = wave; t < ntiles; t += 2 * KS) {
-      if (t + KS < ntiles) load_tile(t + KS, std::integral_constant<int, 1>{});
-      compute(std::integral_constant<int, 0>{}, t * BN);
+    if constexpr (STAGE) {
+      // The pair is rewritten from the registers only after the tile in it
+      // has been computed (a wave's LDS accesses complete in order), and the
+      // registers are reloaded only after that write.
+      if (wave + KS < ntiles) stage_tile(wave + KS);
       __builtin_amdgcn_s_waitcnt(kWaitLoads);
-      if (t + KS < ntiles) {
-        if (t + 2 * KS < ntiles) load_tile(t + 2 * KS, std::integral_constant<int, 0>{});
-        compute(std::integral_constant<int, 1>{}, (t + KS) * BN);
+      for (int t = wave;;) {
+        compute(std::integral_constant<int, 0>{}, t * BN);
+        t += KS;
+        if (t >= ntiles) break;
+        unstage_tile();
+        if (t + KS < ntiles) stage_tile(t + KS);
+      }
+    } else {
+      // Reads of a buffer finish (their values feed the products) before the
+      // same wave reloads it two tiles later.  Each step ends by waiting for
+      // its own loads, so a step's reads never wait on the tile it just put
+      // in flight.
+      __builtin_amdgcn_s_waitcnt(kWaitLoads);
+      for (int t = wave; t < ntiles; t += 2 * KS) {
+        if (t + KS < ntiles) load_tile(t + KS, std::integral_constant<int, 1>{});
+        compute(std::integral_constant<int, 0>{}, t * BN);
         __builtin_amdgcn_s_waitcnt(kWaitLoads);
+        if (t + KS < ntiles) {
+          if (t + 2 * KS < ntiles) load_tile(t + 2 * KS, std::integral_constant<int, 0>{});
+          compute(std::integral_constant<int, 1>{}, (t + KS) * BN);
+          __builtin_amdgcn_s_waitcnt(kWaitLoads);
+        }
       }
     }
   }
@@ -274,8 +329,9 @@ __global__ __launch_bounds__(kSplits<D> * 64) void prefill_splitk_kernel(SplitAr
   // Merge (answer-key row A1): waves 1..KS-1 leave their states in LDS,
   // wave 0 rescales every state to the common reference and sums.
   const float l_tot = half_sum(l_run);
+  if constexpr (STAGE) __syncthreads();  // the states go where the tiles were
   if (wave > 0) {
-    float* dst = &mrg[wave - 1][0][0];
+    float* dst = mrg + (wave - 1) * (NREG + 3) * 64;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -289,7 +345,7 @@ __global__ __launch_bounds__(kSplits<D> * 64) void prefill_splitk_kernel(SplitAr
 
   float M = m_run;
 #pragma unroll
-  for (int w = 1; w < KS; ++w) M = fmaxf(M, mrg[w - 1][NREG][lane]);
+  for (int w = 1; w < KS; ++w) M = fmaxf(M, mrg[((w - 1) * (NREG + 3) + NREG) * 64 + lane]);
   const float ref = pinned_ref(M);
   const float w0 = exp2_hw(m_run - ref);  // 0 for an empty state
   float L = l_tot * w0;
@@ -298,7 +354,7 @@ __global__ __launch_bounds__(kSplits<D> * 64) void prefill_splitk_kernel(SplitAr
   for (int nb = 0; nb < NB; ++nb) acc[nb] *= w0;
 #pragma unroll
   for (int w = 1; w < KS; ++w) {
-    const float* src = &mrg[w - 1][0][0];
+    const float* src = mrg + (w - 1) * (NREG + 3) * 64;
     const float ws = exp2_hw(src[NREG * 64 + lane] - ref);
     L = __builtin_fmaf(src[(NREG + 1) * 64 + lane], ws, L);
     mt = fmaxf(mt, src[(NREG + 2) * 64 + lane]);
@@ -350,7 +406,7 @@ hipError_t launch_typed(const Problem& p) {
   a.c = p.scale * kLog2e;
   const int64_t grid = p.B * p.H * a.nrb;
   hipLaunchKernelGGL((prefill_splitk_kernel<T, D, CAUSAL>), dim3((unsigned)grid),
-                     dim3(kSplits<D> * 64), 0, p.stream, a);
+                     dim3(kSplits * 64), 0, p.stream, a);
   return hipGetLastError();
 }
 

@@ -10,8 +10,8 @@
 // One workgroup = 128 threads = 128/TPQ query rows; a row's features are
 // split over TPQ threads (by default TPQ = 2 for D = 128, so a thread keeps
 // at most 64 features of q and 64 of the running output in registers; see
-// kTpqWide for small problems).  Key tiles of 32 rows are staged in LDS and
-// read by broadcast.
+// kTpqWide and kThreadsWide for small problems).  Key tiles of 32 rows are
+// staged in LDS and read by broadcast.
 
 #include <climits>
 
@@ -56,29 +56,35 @@ constexpr int kThreads = 128;
 constexpr int kBNF = 32;
 
 // Threads per query row: the default keeps at most 64 features of q and of
-// the running output per thread; the wide split (8 features per thread)
+// the running output per thread; the wide split (4 features per thread)
 // serves problems too small to fill the GPU, trading a few lane exchanges
-// per key for a quarter to a sixteenth of the serial work per thread.
+// per key for an eighth to a thirty-second of the serial work per thread.
+// Its thread groups are one wave up to D = 64 (so the few rows of a small
+// problem spread over more CUs, each SIMD running one wave) and two at
+// D = 128.  Measured against 8 features per thread and 128-thread groups:
+// B1 H1 N128 D64 9.4 -> 6.9 us, B1 H2 N512 D128 causal 51 -> 44 us.
 template <int D>
 constexpr int kTpqDefault = D > 64 ? 2 : 1;
 template <int D>
-constexpr int kTpqWide = D / 8;
+constexpr int kTpqWide = D / 4;
+template <int D>
+constexpr int kThreadsWide = D > 64 ? 128 : 64;
 // Key-split groups of the wide split (two for D = 128, whose four-group
 // workgroup would need more than 256 registers per thread in dropout mode).
 template <int D>
 constexpr int kKsfWide = D > 64 ? 2 : 4;
 
-// KSF groups of kThreads threads split the key tiles of the workgroup's rows
+// KSF groups of NT threads split the key tiles of the workgroup's rows
 // (group g takes tiles t_first + g, t_first + g + KSF, ...) and merge their
 // states at the end (answer-key row A1); KSF = 1 streams every tile in one
 // group.
-template <int D, int TPQ, bool CAUSAL, int MODE, int KSF>
-__global__ __launch_bounds__(kThreads * KSF) void prefill_f32_kernel(F32Args a) {
+template <int D, int TPQ, bool CAUSAL, int MODE, int KSF, int NT>
+__global__ __launch_bounds__(NT * KSF) void prefill_f32_kernel(F32Args a) {
   constexpr bool VARLEN = MODE == kModeVarlen;
   constexpr bool MASKED = MODE == kModeMasked;
   constexpr bool DROPOUT = MODE == kModeDropout;
   constexpr int DT = D / TPQ;
-  constexpr int QPB = kThreads / TPQ;
+  constexpr int QPB = NT / TPQ;
   constexpr int BN = kBNF;
 
   __shared__ __attribute__((aligned(16))) float Ksm[KSF][BN * D];
@@ -114,8 +120,8 @@ __global__ __launch_bounds__(kThreads * KSF) void prefill_f32_kernel(F32Args a) 
   const float* __restrict__ Vh = a.v + kbase;
   float* __restrict__ Oh = a.o + qbase;
 
-  const int tid = threadIdx.x % kThreads;
-  const int grp = threadIdx.x / kThreads;
+  const int tid = threadIdx.x % NT;
+  const int grp = threadIdx.x / NT;
   float* __restrict__ Ks = Ksm[grp];
   float* __restrict__ Vs = Vsm[grp];
   const int part = tid % TPQ;
@@ -148,7 +154,7 @@ __global__ __launch_bounds__(kThreads * KSF) void prefill_f32_kernel(F32Args a) 
     const int j0 = t * BN;
     // Stage the tile: 16-byte loads, rows past Nk zero.
 #pragma unroll 4
-    for (int e = tid; live && e < BN * D / 4; e += kThreads) {
+    for (int e = tid; live && e < BN * D / 4; e += NT) {
       const int row = e / (D / 4), col = e - row * (D / 4);
       const int j = j0 + row;
       f32x4 kv = f32x4{}, vv = f32x4{};
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(kThreads * KSF) void prefill_f32_kernel(F32Args a) 
   if constexpr (KSF > 1) {
     // Merge (answer-key row A1): groups 1..KSF-1 leave (m, l, acc) in LDS;
     // group 0 rescales each state to the common reference and sums.
-    __shared__ float mst[KSF - 1][DT + 2][kThreads];
+    __shared__ float mst[KSF - 1][DT + 2][NT];
     if (grp > 0) {
       mst[grp - 1][0][tid] = m_run;
       mst[grp - 1][1][tid] = l_run;
@@ -265,9 +271,9 @@ __global__ __launch_bounds__(kThreads * KSF) void prefill_f32_kernel(F32Args a) 
   }
 }
 
-template <int D, int TPQ, bool CAUSAL, int MODE, int KSF>
+template <int D, int TPQ, bool CAUSAL, int MODE, int KSF, int NT>
 hipError_t launch_typed(const Problem& p) {
-  constexpr int QPB = kThreads / TPQ;
+  constexpr int QPB = NT / TPQ;
   F32Args a;
   a.q = static_cast<const float*>(p.q);
   a.k = static_cast<const float*>(p.k);
@@ -296,24 +302,24 @@ hipError_t launch_typed(const Problem& p) {
   a.drop_t = p.drop_t;
   a.keep_gain = (float)(65536.0 / (65536.0 - (double)p.drop_t));
   const int64_t grid = p.B * p.H * a.nqt;
-  hipLaunchKernelGGL((prefill_f32_kernel<D, TPQ, CAUSAL, MODE, KSF>), dim3((unsigned)grid), dim3(kThreads * KSF), 0,
+  hipLaunchKernelGGL((prefill_f32_kernel<D, TPQ, CAUSAL, MODE, KSF, NT>), dim3((unsigned)grid), dim3(NT * KSF), 0,
                      p.stream, a);
   return hipGetLastError();
 }
 
-template <int D, int TPQ, int KSF>
+template <int D, int TPQ, int KSF, int NT>
 hipError_t launch_mode(const Problem& p) {
   if (p.cu_q)
-    return p.causal ? launch_typed<D, TPQ, true, kModeVarlen, KSF>(p)
-                    : launch_typed<D, TPQ, false, kModeVarlen, KSF>(p);
+    return p.causal ? launch_typed<D, TPQ, true, kModeVarlen, KSF, NT>(p)
+                    : launch_typed<D, TPQ, false, kModeVarlen, KSF, NT>(p);
   if (p.mask || p.window > 0)
-    return p.causal ? launch_typed<D, TPQ, true, kModeMasked, KSF>(p)
-                    : launch_typed<D, TPQ, false, kModeMasked, KSF>(p);
+    return p.causal ? launch_typed<D, TPQ, true, kModeMasked, KSF, NT>(p)
+                    : launch_typed<D, TPQ, false, kModeMasked, KSF, NT>(p);
   if (p.dropout)
-    return p.causal ? launch_typed<D, TPQ, true, kModeDropout, KSF>(p)
-                    : launch_typed<D, TPQ, false, kModeDropout, KSF>(p);
-  return p.causal ? launch_typed<D, TPQ, true, kModeBatched, KSF>(p)
-                  : launch_typed<D, TPQ, false, kModeBatched, KSF>(p);
+    return p.causal ? launch_typed<D, TPQ, true, kModeDropout, KSF, NT>(p)
+                    : launch_typed<D, TPQ, false, kModeDropout, KSF, NT>(p);
+  return p.causal ? launch_typed<D, TPQ, true, kModeBatched, KSF, NT>(p)
+                  : launch_typed<D, TPQ, false, kModeBatched, KSF, NT>(p);
 }
 
 template <int D>
@@ -323,8 +329,8 @@ hipError_t launch_d(const Problem& p) {
   // depends only on (B, H, Nq), so every mode of one problem shape splits
   // its rows the same way and computes each row identically.
   constexpr int64_t qpb = kThreads / kTpqDefault<D>;
-  if (p.B * p.H * ((p.Nq + qpb - 1) / qpb) < 128) return launch_mode<D, kTpqWide<D>, kKsfWide<D>>(p);
-  return launch_mode<D, kTpqDefault<D>, 1>(p);
+  if (p.B * p.H * ((p.Nq + qpb - 1) / qpb) < 128) return launch_mode<D, kTpqWide<D>, kKsfWide<D>, kThreadsWide<D>>(p);
+  return launch_mode<D, kTpqDefault<D>, 1, kThreads>(p);
 }
 
 }  // namespace

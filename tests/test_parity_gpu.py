@@ -374,12 +374,14 @@ def test_online_merge_batch_matches_oracle():
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("nq,nk,d", [(259, 259, 128), (130, 333, 64), (333, 130, 64),
                                      (64, 64, 32), (700, 700, 16), (40, 2000, 64),
-                                     (100, 1000, 128)])
+                                     (100, 1000, 128), (64, 4099, 128)])
 def test_small_grid_split_and_wide_grid(dtype, causal, nq, nk, d):
     # A problem with few workgroups splits the keys of each 32-row block over
     # the waves of a workgroup and merges their states; a large one streams
     # them in one wave.  Both are checked against the oracle: the small
     # problem in full, the same heads repeated 64 times on three repeats.
+    # At D = 128 the split waves stage each next tile in registers: 4099
+    # keys give a wave 16 or 17 tiles, the last one ragged.
     _say(f"grid variants dtype={dtype} causal={causal} Nq={nq} Nk={nk} D={d}")
     q, k, v = random_qkv(1, 2, nq, nk, d, dtype, seed=nq + 7 * nk + d, device=DEV, k_ramp=0.01)
     scale = default_scale(d)
@@ -420,7 +422,7 @@ def test_sixteen_wave_noncausal_d64(dtype, nq, nk):
 @pytest.mark.parametrize("nq,nk,d", [(259, 259, 128), (130, 333, 64), (333, 130, 32),
                                      (100, 100, 16)])
 def test_fp32_small_grid_split_and_default_split(causal, nq, nk, d):
-    # FP32 problems with few workgroups split each row over D/8 threads,
+    # FP32 problems with few workgroups split each row over D/4 threads,
     # large ones over 1 or 2.  The summation order differs, so both are
     # checked against the oracle: the small problem in full, the same heads
     # repeated 64 times on three of the repeats.

@@ -10,8 +10,8 @@
 // One workgroup = 128 threads = 128/TPQ query rows; a row's features are
 // split over TPQ threads (by default TPQ = 2 for D = 128, so a thread keeps
 // at most 64 features of q and 64 of the running output in registers; see
-// kTpqWide and kThreadsWide for small problems).  Key tiles of 32 rows are
-// staged in LDS and read by broadcast.
+// kTpqWide and kThreadsWide for small problems).  Key tiles of 32 rows (16
+// in the wide split up to D = 64) are staged in LDS and read by broadcast.
 
 #include <climits>
 
@@ -69,23 +69,27 @@ template <int D>
 constexpr int kTpqWide = D / 4;
 template <int D>
 constexpr int kThreadsWide = D > 64 ? 128 : 64;
-// Key-split groups of the wide split (two for D = 128, whose four-group
-// workgroup would need more than 256 registers per thread in dropout mode).
+// Key-split groups of the wide split and their key tiles: eight groups of
+// 16-key tiles up to D = 64 (against four of 32 keys: B1 H1 N128 D64 causal
+// 7.1 -> 6.2 us, B1 H1 N1024 causal 41 -> 27 us), two of 32 keys at D = 128,
+// whose four-group workgroup would need more than 256 registers per thread
+// in dropout mode.
 template <int D>
-constexpr int kKsfWide = D > 64 ? 2 : 4;
+constexpr int kKsfWide = D > 64 ? 2 : 8;
+template <int D>
+constexpr int kBnWide = D > 64 ? 32 : 16;
 
 // KSF groups of NT threads split the key tiles of the workgroup's rows
 // (group g takes tiles t_first + g, t_first + g + KSF, ...) and merge their
 // states at the end (answer-key row A1); KSF = 1 streams every tile in one
 // group.
-template <int D, int TPQ, bool CAUSAL, int MODE, int KSF, int NT>
+template <int D, int TPQ, bool CAUSAL, int MODE, int KSF, int NT, int BN>
 __global__ __launch_bounds__(NT * KSF) void prefill_f32_kernel(F32Args a) {
   constexpr bool VARLEN = MODE == kModeVarlen;
   constexpr bool MASKED = MODE == kModeMasked;
   constexpr bool DROPOUT = MODE == kModeDropout;
   constexpr int DT = D / TPQ;
   constexpr int QPB = NT / TPQ;
-  constexpr int BN = kBNF;
 
   __shared__ __attribute__((aligned(16))) float Ksm[KSF][BN * D];
   __shared__ __attribute__((aligned(16))) float Vsm[KSF][BN * D];
@@ -171,11 +175,12 @@ __global__ __launch_bounds__(NT * KSF) void prefill_f32_kernel(F32Args a) {
       continue;
     }
 
-    // The row's mask bits for keys j0 .. j0+31 (all set without a mask) and
+    // The row's mask bits for keys j0 .. j0+BN-1 from bit 0 on (all set
+    // without a mask; a 16-key tile starts at bit 0 or 16 of its word) and
     // the window's lower limit (visible iff j > wlo), one compare per key.
     const int wlo = win > 0 ? qrow + off - win : INT_MIN;
     uint32_t mw = ~0u;
-    if (MASKED && a.mask) mw = mrow && j0 / 32 < a.mask_words ? mrow[j0 / 32] : 0u;
+    if (MASKED && a.mask) mw = mrow && j0 / 32 < a.mask_words ? mrow[j0 / 32] >> (j0 & 31) : 0u;
     float s[BN];
     float mx = kNegInf;
 #pragma unroll
@@ -204,8 +209,8 @@ __global__ __launch_bounds__(NT * KSF) void prefill_f32_kernel(F32Args a) {
     }
     l_run = l_run * alpha + rs;
     if (DROPOUT) {
-      // Keys j0 .. j0+31 are fields of Philox blocks j0/16 and j0/16 + 1 of
-      // this row (counter (j / 16, i, bh, offset), key (seed, 0)).
+      // Keys j0 .. j0+BN-1 are fields of Philox blocks j0/16, ... of this
+      // row (counter (j / 16, i, bh, offset), key (seed, 0)).
 #pragma unroll
       for (int blk = 0; blk < BN / 16; ++blk) {
         uint64_t w[4] = {(uint64_t)((j0 >> 4) + blk), (uint64_t)qrow, (uint64_t)bh, a.offset};
@@ -271,7 +276,7 @@ __global__ __launch_bounds__(NT * KSF) void prefill_f32_kernel(F32Args a) {
   }
 }
 
-template <int D, int TPQ, bool CAUSAL, int MODE, int KSF, int NT>
+template <int D, int TPQ, bool CAUSAL, int MODE, int KSF, int NT, int BN>
 hipError_t launch_typed(const Problem& p) {
   constexpr int QPB = NT / TPQ;
   F32Args a;
@@ -302,24 +307,24 @@ hipError_t launch_typed(const Problem& p) {
   a.drop_t = p.drop_t;
   a.keep_gain = (float)(65536.0 / (65536.0 - (double)p.drop_t));
   const int64_t grid = p.B * p.H * a.nqt;
-  hipLaunchKernelGGL((prefill_f32_kernel<D, TPQ, CAUSAL, MODE, KSF, NT>), dim3((unsigned)grid), dim3(NT * KSF), 0,
+  hipLaunchKernelGGL((prefill_f32_kernel<D, TPQ, CAUSAL, MODE, KSF, NT, BN>), dim3((unsigned)grid), dim3(NT * KSF), 0,
                      p.stream, a);
   return hipGetLastError();
 }
 
-template <int D, int TPQ, int KSF, int NT>
+template <int D, int TPQ, int KSF, int NT, int BN>
 hipError_t launch_mode(const Problem& p) {
   if (p.cu_q)
-    return p.causal ? launch_typed<D, TPQ, true, kModeVarlen, KSF, NT>(p)
-                    : launch_typed<D, TPQ, false, kModeVarlen, KSF, NT>(p);
+    return p.causal ? launch_typed<D, TPQ, true, kModeVarlen, KSF, NT, BN>(p)
+                    : launch_typed<D, TPQ, false, kModeVarlen, KSF, NT, BN>(p);
   if (p.mask || p.window > 0)
-    return p.causal ? launch_typed<D, TPQ, true, kModeMasked, KSF, NT>(p)
-                    : launch_typed<D, TPQ, false, kModeMasked, KSF, NT>(p);
+    return p.causal ? launch_typed<D, TPQ, true, kModeMasked, KSF, NT, BN>(p)
+                    : launch_typed<D, TPQ, false, kModeMasked, KSF, NT, BN>(p);
   if (p.dropout)
-    return p.causal ? launch_typed<D, TPQ, true, kModeDropout, KSF, NT>(p)
-                    : launch_typed<D, TPQ, false, kModeDropout, KSF, NT>(p);
-  return p.causal ? launch_typed<D, TPQ, true, kModeBatched, KSF, NT>(p)
-                  : launch_typed<D, TPQ, false, kModeBatched, KSF, NT>(p);
+    return p.causal ? launch_typed<D, TPQ, true, kModeDropout, KSF, NT, BN>(p)
+                    : launch_typed<D, TPQ, false, kModeDropout, KSF, NT, BN>(p);
+  return p.causal ? launch_typed<D, TPQ, true, kModeBatched, KSF, NT, BN>(p)
+                  : launch_typed<D, TPQ, false, kModeBatched, KSF, NT, BN>(p);
 }
 
 template <int D>
@@ -329,8 +334,8 @@ hipError_t launch_d(const Problem& p) {
   // depends only on (B, H, Nq), so every mode of one problem shape splits
   // its rows the same way and computes each row identically.
   constexpr int64_t qpb = kThreads / kTpqDefault<D>;
-  if (p.B * p.H * ((p.Nq + qpb - 1) / qpb) < 128) return launch_mode<D, kTpqWide<D>, kKsfWide<D>, kThreadsWide<D>>(p);
-  return launch_mode<D, kTpqDefault<D>, 1, kThreads>(p);
+  if (p.B * p.H * ((p.Nq + qpb - 1) / qpb) < 128) return launch_mode<D, kTpqWide<D>, kKsfWide<D>, kThreadsWide<D>, kBnWide<D>>(p);
+  return launch_mode<D, kTpqDefault<D>, 1, kThreads, kBNF>(p);
 }
 
 }  // namespace

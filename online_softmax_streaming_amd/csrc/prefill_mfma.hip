@@ -764,10 +764,16 @@ hipError_t launch_typed(const Problem& p) {
 #define ATTN_PREFILL_WAVES 8
 #endif
 constexpr int kWaves = ATTN_PREFILL_WAVES;
-// Below a quarter of the 256 CUs in workgroups the key-split kernel wins;
-// from 64 up, per-workgroup chains are long enough that the eight-wave
-// kernel does (B1 H4 N8192 D128 causal: 192 us here, 258 us split).
-constexpr int64_t kSmallGridWgs = 64;
+// Up to this many eight-wave workgroups the key-split kernel wins; beyond,
+// per-workgroup chains are long enough that the eight-wave kernel does.
+// D = 128: below 64 (B1 H4 N16384 causal, 128 workgroups: 362 us here, 567
+// split; at 64 workgroups the two trade places by shape).  D = 64: up to 64
+// (B1 H8 N2048 noncausal, 64 workgroups: 22.5 us split, 35.7 here; at 96
+// and 128 this kernel mostly wins).  D <= 32: up to 128 (B2 H8 N2048 D32
+// noncausal, 128 workgroups: 20.9 us split, 29.4 here; at 256 this kernel
+// wins).
+template <int D>
+constexpr int64_t kSmallGridWgs = D > 64 ? 63 : D == 64 ? 64 : 128;
 constexpr int64_t kNumCUs = 256;
 
 template <typename T, int D>
@@ -781,12 +787,12 @@ hipError_t launch_d(const Problem& p) {
   if (p.dropout)
     return p.causal ? launch_typed<T, D, kWaves, true, kModeDropout>(p)
                     : launch_typed<T, D, kWaves, false, kModeDropout>(p);
-  // A small problem (fewer workgroups of kWaves waves than a quarter of the CUs)
-  // splits the keys of each 32-row block over the waves of a workgroup
+  // A small problem (few workgroups of kWaves waves, kSmallGridWgs) splits
+  // the keys of each 32-row block over the waves of a workgroup
   // (prefill_splitk.hip): more waves busy, each with a shorter chain.
   const int64_t nqt = (p.Nq + 32 * kWaves - 1) / (32 * kWaves);
   const int64_t wgs = p.B * p.H * (p.causal ? (nqt + 1) / 2 : nqt);
-  if (wgs < kSmallGridWgs) return launch_prefill_splitk(p);
+  if (wgs <= kSmallGridWgs<D>) return launch_prefill_splitk(p);
   if constexpr (D == 64) {
     // Noncausal D = 64 whose eight-wave grid would put a second workgroup
     // on some CUs while sixteen-wave workgroups (512 rows) fit one per CU:

@@ -379,23 +379,43 @@ def test_small_grid_split_and_wide_grid(dtype, causal, nq, nk, d):
     # A problem with few workgroups splits the keys of each 32-row block over
     # the waves of a workgroup and merges their states; a large one streams
     # them in one wave.  Both are checked against the oracle: the small
-    # problem in full, the same heads repeated 64 times on three repeats.
-    # At D = 128 the split waves stage each next tile in registers: 4099
-    # keys give a wave 16 or 17 tiles, the last one ragged.
+    # problem in full, the same heads repeated 96 times (at least 192
+    # eight-wave workgroups, above every head size's split threshold) on
+    # three repeats.  At D = 128 the split waves stage each next tile in
+    # registers: 4099 keys give a wave 16 or 17 tiles, the last one ragged.
     _say(f"grid variants dtype={dtype} causal={causal} Nq={nq} Nk={nk} D={d}")
     q, k, v = random_qkv(1, 2, nq, nk, d, dtype, seed=nq + 7 * nk + d, device=DEV, k_ramp=0.01)
     scale = default_scale(d)
     small, sm, sl = attn_fwd_stats(q, k, v, causal=causal, scale=scale)
-    wide, wm, wl = attn_fwd_stats(q.repeat(64, 1, 1, 1), k.repeat(64, 1, 1, 1),
-                                  v.repeat(64, 1, 1, 1), causal=causal, scale=scale)
+    wide, wm, wl = attn_fwd_stats(q.repeat(96, 1, 1, 1), k.repeat(96, 1, 1, 1),
+                                  v.repeat(96, 1, 1, 1), causal=causal, scale=scale)
     again = attn_fwd(q, k, v, causal=causal, scale=scale)
     torch.cuda.synchronize()
     assert torch.equal(again, small), "the split path is not deterministic"
     err = _compare_full(q, k, v, causal, scale, small, TOL[dtype], sm, sl)
     _record(f"small grid {dtype} causal={causal} D={d} Nq={nq} Nk={nk}", err, TOL[dtype])
-    for rep in (0, 37, 63):
+    for rep in (0, 47, 95):
         _compare_full(q, k, v, causal, scale, wide[rep:rep + 1], TOL[dtype], wm[rep:rep + 1],
                       wl[rep:rep + 1])
+
+
+@pytest.mark.parametrize("b,h,n,d,causal", [(1, 8, 2048, 64, False), (2, 4, 4096, 64, True),
+                                             (2, 8, 2048, 32, False), (4, 8, 2048, 16, True)])
+def test_split_path_at_its_threshold(b, h, n, d, causal):
+    # Problems with as many eight-wave workgroups as the key-split path still
+    # takes for their head size (64 at D = 64, 128 at D <= 32): heads 0 and
+    # the last one compared in full.
+    _say(f"split threshold B={b} H={h} N={n} D={d} causal={causal}")
+    q, k, v = random_qkv(b, h, n, n, d, "bf16", seed=n + d, device=DEV, k_ramp=0.002)
+    scale = default_scale(d)
+    out, m, l = attn_fwd_stats(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    err = 0.0
+    for bi, hi in [(0, 0), (b - 1, h - 1)]:
+        sl = (slice(bi, bi + 1), slice(hi, hi + 1))
+        err = max(err, _compare_full(q[sl], k[sl], v[sl], causal, scale, out[sl], TOL["bf16"],
+                                     m[sl], l[sl]))
+    _record(f"split threshold B={b} H={h} N={n} D={d} causal={causal}", err, TOL["bf16"])
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])

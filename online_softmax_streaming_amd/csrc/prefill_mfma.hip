@@ -765,34 +765,53 @@ hipError_t launch_typed(const Problem& p) {
 #endif
 constexpr int kWaves = ATTN_PREFILL_WAVES;
 // Up to this many eight-wave workgroups the key-split kernel wins; beyond,
-// per-workgroup chains are long enough that the eight-wave kernel does.
-// D = 128: below 64 (B1 H4 N16384 causal, 128 workgroups: 362 us here, 567
-// split; at 64 workgroups the two trade places by shape).  D = 64: up to 64
-// (B1 H8 N2048 noncausal, 64 workgroups: 22.5 us split, 35.7 here; at 96
-// and 128 this kernel mostly wins).  D <= 32: up to 128 (B2 H8 N2048 D32
-// noncausal, 128 workgroups: 20.9 us split, 29.4 here; at 256 this kernel
-// wins).
+// per-workgroup chains are long enough that the tiled kernel (with four-wave
+// workgroups up to half the CUs) does.  D = 128: below 64 (B1 H2 N4096
+// causal, 16 workgroups: 36 us split, 75 tiled; at 64 the two trade places
+// by shape).  D <= 64: up to 64 (B2 H8 N2048 D32 causal, 64 workgroups: 21.0
+// us split, 25.5 tiled; B1 H4 N4096 D64 causal, 32: 36 against 52; at 128
+// the four-wave kernel is level or ahead, B4 H8 N2048 D16 causal 21.9
+// against 27.0 us).
 template <int D>
-constexpr int64_t kSmallGridWgs = D > 64 ? 63 : D == 64 ? 64 : 128;
+constexpr int64_t kSmallGridWgs = D > 64 ? 63 : 64;
 constexpr int64_t kNumCUs = 256;
+
+// Every layout of one workgroup size.
+template <typename T, int D, int NW>
+hipError_t launch_nw(const Problem& p) {
+  if (p.cu_q)
+    return p.causal ? launch_typed<T, D, NW, true, kModeVarlen>(p)
+                    : launch_typed<T, D, NW, false, kModeVarlen>(p);
+  if (p.mask || p.window > 0)
+    return p.causal ? launch_typed<T, D, NW, true, kModeMasked>(p)
+                    : launch_typed<T, D, NW, false, kModeMasked>(p);
+  if (p.dropout)
+    return p.causal ? launch_typed<T, D, NW, true, kModeDropout>(p)
+                    : launch_typed<T, D, NW, false, kModeDropout>(p);
+  return p.causal ? launch_typed<T, D, NW, true, kModeBatched>(p)
+                  : launch_typed<T, D, NW, false, kModeBatched>(p);
+}
 
 template <typename T, int D>
 hipError_t launch_d(const Problem& p) {
-  if (p.cu_q)
-    return p.causal ? launch_typed<T, D, kWaves, true, kModeVarlen>(p)
-                    : launch_typed<T, D, kWaves, false, kModeVarlen>(p);
-  if (p.mask || p.window > 0)
-    return p.causal ? launch_typed<T, D, kWaves, true, kModeMasked>(p)
-                    : launch_typed<T, D, kWaves, false, kModeMasked>(p);
-  if (p.dropout)
-    return p.causal ? launch_typed<T, D, kWaves, true, kModeDropout>(p)
-                    : launch_typed<T, D, kWaves, false, kModeDropout>(p);
-  // A small problem (few workgroups of kWaves waves, kSmallGridWgs) splits
-  // the keys of each 32-row block over the waves of a workgroup
-  // (prefill_splitk.hip): more waves busy, each with a shorter chain.
+  // Workgroups of kWaves waves the problem would take (varlen: with every
+  // sequence as long as the longest).  The choices below depend only on
+  // (B, H, Nq, D, causal), so the layouts of one problem (plain, varlen,
+  // masked, dropout) split their rows alike and agree bit for bit where
+  // their arithmetic does.
   const int64_t nqt = (p.Nq + 32 * kWaves - 1) / (32 * kWaves);
   const int64_t wgs = p.B * p.H * (p.causal ? (nqt + 1) / 2 : nqt);
-  if (wgs <= kSmallGridWgs<D>) return launch_prefill_splitk(p);
+  const bool plain = !p.cu_q && !p.mask && p.window <= 0 && !p.dropout;
+  // A small problem (few workgroups, kSmallGridWgs) splits the keys of each
+  // 32-row block over the waves of a workgroup (prefill_splitk.hip): more
+  // waves busy, each with a shorter chain.
+  if (plain && wgs <= kSmallGridWgs<D>) return launch_prefill_splitk(p);
+  // A grid that would fill at most half the CUs takes four-wave workgroups
+  // (128 rows): twice as many, one per CU, each SIMD running one wave.  B1
+  // H8 N8192 D64 causal 137 -> 97 us, B1 H4 N16384 D128 causal 363 -> 280
+  // us, B1 H8 N4096 D128 noncausal 93 -> 73 us; with 256 eight-wave
+  // workgroups they lose (B2 H8 N4096 D128 noncausal 122 -> 129 us).
+  if (wgs <= kNumCUs / 2) return launch_nw<T, D, 4>(p);
   if constexpr (D == 64) {
     // Noncausal D = 64 whose eight-wave grid would put a second workgroup
     // on some CUs while sixteen-wave workgroups (512 rows) fit one per CU:
@@ -800,11 +819,10 @@ hipError_t launch_d(const Problem& p) {
     // (B3 H8 N4099 f16: 780 against 730 TFLOP/s; shapes that fill the GPU
     // several times over are level, small ones lose and keep eight waves).
     const int64_t wgs16 = p.B * p.H * ((p.Nq + 511) / 512);
-    if (!p.causal && wgs > kNumCUs && wgs16 <= kNumCUs)
+    if (plain && !p.causal && wgs > kNumCUs && wgs16 <= kNumCUs)
       return launch_typed<T, D, 16, false, kModeBatched>(p);
   }
-  return p.causal ? launch_typed<T, D, kWaves, true, kModeBatched>(p)
-                  : launch_typed<T, D, kWaves, false, kModeBatched>(p);
+  return launch_nw<T, D, kWaves>(p);
 }
 
 template <typename T>

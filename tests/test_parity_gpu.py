@@ -380,8 +380,8 @@ def test_small_grid_split_and_wide_grid(dtype, causal, nq, nk, d):
     # the waves of a workgroup and merges their states; a large one streams
     # them in one wave.  Both are checked against the oracle: the small
     # problem in full, the same heads repeated 96 times (at least 192
-    # eight-wave workgroups, above every head size's split threshold) on
-    # three repeats.  At D = 128 the split waves stage each next tile in
+    # eight-wave workgroups, which take eight-wave workgroups of the tiled
+    # kernel) on three repeats.  At D = 128 the split waves stage each next tile in
     # registers: 4099 keys give a wave 16 or 17 tiles, the last one ragged.
     _say(f"grid variants dtype={dtype} causal={causal} Nq={nq} Nk={nk} D={d}")
     q, k, v = random_qkv(1, 2, nq, nk, d, dtype, seed=nq + 7 * nk + d, device=DEV, k_ramp=0.01)
@@ -399,23 +399,27 @@ def test_small_grid_split_and_wide_grid(dtype, causal, nq, nk, d):
                       wl[rep:rep + 1])
 
 
-@pytest.mark.parametrize("b,h,n,d,causal", [(1, 8, 2048, 64, False), (2, 4, 4096, 64, True),
-                                             (2, 8, 2048, 32, False), (4, 8, 2048, 16, True)])
-def test_split_path_at_its_threshold(b, h, n, d, causal):
-    # Problems with as many eight-wave workgroups as the key-split path still
-    # takes for their head size (64 at D = 64, 128 at D <= 32): heads 0 and
-    # the last one compared in full.
-    _say(f"split threshold B={b} H={h} N={n} D={d} causal={causal}")
-    q, k, v = random_qkv(b, h, n, n, d, "bf16", seed=n + d, device=DEV, k_ramp=0.002)
+@pytest.mark.parametrize("b,h,n,d,causal,dtype", [
+    # 64 eight-wave workgroups, the most the key-split path takes at D <= 64.
+    (1, 8, 2048, 64, False, "bf16"), (2, 4, 4096, 64, True, "bf16"),
+    (2, 8, 2048, 32, True, "bf16"), (2, 4, 2048, 16, False, "f16"),
+    # 65 to 128 eight-wave workgroups: four-wave workgroups of 128 rows.
+    (1, 8, 8192, 64, True, "bf16"), (1, 8, 4096, 128, False, "bf16"),
+    (1, 12, 2048, 64, False, "f16"), (2, 4, 4100, 128, True, "bf16")])
+def test_grid_size_paths(b, h, n, d, causal, dtype):
+    # The paths the launch takes by grid size, at their boundaries: heads 0
+    # and the last one compared in full.
+    _say(f"grid-size path B={b} H={h} N={n} D={d} causal={causal} {dtype}")
+    q, k, v = random_qkv(b, h, n, n, d, dtype, seed=n + d, device=DEV, k_ramp=0.002)
     scale = default_scale(d)
     out, m, l = attn_fwd_stats(q, k, v, causal=causal, scale=scale)
     torch.cuda.synchronize()
     err = 0.0
     for bi, hi in [(0, 0), (b - 1, h - 1)]:
         sl = (slice(bi, bi + 1), slice(hi, hi + 1))
-        err = max(err, _compare_full(q[sl], k[sl], v[sl], causal, scale, out[sl], TOL["bf16"],
+        err = max(err, _compare_full(q[sl], k[sl], v[sl], causal, scale, out[sl], TOL[dtype],
                                      m[sl], l[sl]))
-    _record(f"split threshold B={b} H={h} N={n} D={d} causal={causal}", err, TOL["bf16"])
+    _record(f"grid-size path B={b} H={h} N={n} D={d} causal={causal} {dtype}", err, TOL[dtype])
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])

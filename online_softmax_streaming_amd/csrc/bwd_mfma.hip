@@ -736,8 +736,18 @@ hipError_t launch_typed(const BwdProblem& p, float* stat) {
   if (p.Nq > 0) {
     constexpr int BM = 32 * kQWaves;
     fill_grid(a, p.B * p.H, (int)((p.Nq + BM - 1) / BM), CAUSAL, &grid);
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, kQWaves, CAUSAL>), dim3((unsigned)grid),
-                       dim3(kQWaves * 64), 0, p.stream, a);
+    if (a.total <= 128) {
+      // A dQ grid that would fill at most half the CUs takes four-wave
+      // workgroups (128 rows), twice as many: B1 H8 N4096 D128 causal 267
+      // -> 222 us per backward, B1 H4 N8192 causal 478 -> 397 us; with 256
+      // or more eight-wave workgroups the two are level.
+      fill_grid(a, p.B * p.H, (int)((p.Nq + 127) / 128), CAUSAL, &grid);
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, 4, CAUSAL>), dim3((unsigned)grid), dim3(4 * 64), 0,
+                         p.stream, a);
+    } else {
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, kQWaves, CAUSAL>), dim3((unsigned)grid),
+                         dim3(kQWaves * 64), 0, p.stream, a);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -329,12 +329,17 @@ hipError_t launch_mode(const Problem& p) {
 
 template <int D>
 hipError_t launch_d(const Problem& p) {
-  // Fewer default workgroups than half the CUs: the wide split, with the
-  // key tiles shared out over kKsfWide thread groups.  The rule
-  // depends only on (B, H, Nq), so every mode of one problem shape splits
-  // its rows the same way and computes each row identically.
+  // Fewer than 512 default workgroups (of two waves each, at most one wave
+  // per SIMD): the wide split, with the key tiles shared out over kKsfWide
+  // thread groups (against the default: B1 H8 N2048 D64 noncausal, 128
+  // workgroups, 1118 -> 594 us; B1 H8 N4096 D64 causal, 256, 2179 -> 1254
+  // us; B2 H4 N4096 D32 noncausal 1169 -> 897 us; at 512 and more the
+  // default kernel wins).  The rule depends only on (B, H, Nq), so every
+  // mode of one problem shape splits its rows the same way and computes
+  // each row identically.
   constexpr int64_t qpb = kThreads / kTpqDefault<D>;
-  if (p.B * p.H * ((p.Nq + qpb - 1) / qpb) < 128) return launch_mode<D, kTpqWide<D>, kKsfWide<D>, kThreadsWide<D>, kBnWide<D>>(p);
+  if (p.B * p.H * ((p.Nq + qpb - 1) / qpb) < 512)
+    return launch_mode<D, kTpqWide<D>, kKsfWide<D>, kThreadsWide<D>, kBnWide<D>>(p);
   return launch_mode<D, kTpqDefault<D>, 1, kThreads, kBNF>(p);
 }
 

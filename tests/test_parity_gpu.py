@@ -449,16 +449,17 @@ def test_fp32_small_grid_split_and_default_split(causal, nq, nk, d):
     # FP32 problems with few workgroups split each row over D/4 threads,
     # large ones over 1 or 2.  The summation order differs, so both are
     # checked against the oracle: the small problem in full, the same heads
-    # repeated 64 times on three of the repeats.
+    # repeated 256 times (at least 512 default workgroups) on three of the
+    # repeats.
     _say(f"fp32 grid variants causal={causal} Nq={nq} Nk={nk} D={d}")
     q, k, v = random_qkv(1, 2, nq, nk, d, "f32", seed=nq + 3 * nk + d, device=DEV, k_ramp=0.01)
     scale = default_scale(d)
     small, sm, sl = attn_fwd_stats(q, k, v, causal=causal, scale=scale)
-    wide, wm, wl = attn_fwd_stats(q.repeat(64, 1, 1, 1), k.repeat(64, 1, 1, 1),
-                                  v.repeat(64, 1, 1, 1), causal=causal, scale=scale)
+    wide, wm, wl = attn_fwd_stats(q.repeat(256, 1, 1, 1), k.repeat(256, 1, 1, 1),
+                                  v.repeat(256, 1, 1, 1), causal=causal, scale=scale)
     torch.cuda.synchronize()
     err = _compare_full(q, k, v, causal, scale, small, TOL["f32"], sm, sl)
     _record(f"fp32 small grid causal={causal} D={d} Nq={nq} Nk={nk}", err, TOL["f32"])
-    for rep in (0, 37, 63):
+    for rep in (0, 137, 255):
         _compare_full(q, k, v, causal, scale, wide[rep:rep + 1], TOL["f32"], wm[rep:rep + 1],
                       wl[rep:rep + 1])

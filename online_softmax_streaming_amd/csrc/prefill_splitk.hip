@@ -42,6 +42,8 @@ struct SplitArgs {
   int Nq, Nk;
   int group;  // query heads per K/V head
   int nrb;    // 32-row query blocks per (b, h)
+  int total;    // B * H * nrb workgroups of work
+  int per_xcd;  // gridDim.x / 8 when workgroups are regrouped by XCD, else 0
   float c;    // scale * log2(e)
 };
 
@@ -97,8 +99,17 @@ __global__ __launch_bounds__(kSplits * 64) void prefill_splitk_kernel(SplitArgs 
     return buf == 0 ? &buf0[(wave * 2 + kv) * TILE] : &buf1[(wave * 2 + kv) * TILE];
   };
 
-  const int bh = blockIdx.x / a.nrb;
-  const int rb = blockIdx.x - bh * a.nrb;
+  // Consecutive workgroup ids land on different XCDs (round-robin over 8).
+  // When the problem's K/V outgrow one XCD's L2 (4 MB), the ids are
+  // regrouped so each XCD takes a contiguous range of heads: the row blocks
+  // of a head then read its K/V tiles through one L2, about together,
+  // instead of every XCD fetching every head's K/V (B1 H32 Nq256 Nk16384
+  // D128 causal: 322 -> 124 us; B4 H8 Nq256 Nk4096: 81 -> 37 us).
+  const int bid = blockIdx.x;
+  const int logical = a.per_xcd ? (bid & 7) * a.per_xcd + (bid >> 3) : bid;
+  if (logical >= a.total) return;
+  const int bh = logical / a.nrb;
+  const int rb = logical - bh * a.nrb;
   const int Nq = a.Nq, Nk = a.Nk;
   const int off = Nk - Nq;
   const int64_t qbase = (int64_t)bh * Nq * D;
@@ -404,7 +415,11 @@ hipError_t launch_typed(const Problem& p) {
   a.group = (int)(p.H / p.Hkv);
   a.nrb = (int)((p.Nq + 31) / 32);
   a.c = p.scale * kLog2e;
-  const int64_t grid = p.B * p.H * a.nrb;
+  const int64_t total = p.B * p.H * a.nrb;
+  const bool regroup = p.B * p.Hkv * p.Nk * p.D * 4 > ((int64_t)4 << 20);  // K and V bytes
+  const int64_t grid = regroup ? (total + 7) / 8 * 8 : total;
+  a.total = (int)total;
+  a.per_xcd = regroup ? (int)(grid / 8) : 0;
   hipLaunchKernelGGL((prefill_splitk_kernel<T, D, CAUSAL>), dim3((unsigned)grid),
                      dim3(kSplits * 64), 0, p.stream, a);
   return hipGetLastError();

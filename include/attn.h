@@ -91,13 +91,17 @@ extern "C" {
  *
  * Paths: Nq <= 8 takes the split-key decode path (keys split across
  * workgroups, partial states merged); so does bf16/f16 with Nq <= 32,
- * (H / Hkv) * Nq <= 64 and Nk >= 8192.  Everything else takes the tiled
- * prefill kernels.
- * Memory: the prefill path allocates nothing.  The split-key decode path
- * (both routes above) needs a scratch array of partial states, taken
- * stream-ordered with hipMallocAsync / hipFreeAsync on `stream`; under HIP
- * graph capture those become the graph's own allocation nodes.  Callers
- * that cannot allocate at all use attn_decode_paged_noalloc.
+ * (H / Hkv) * Nq <= 64 and Nk >= 8192.  bf16/f16 problems of at most 64
+ * query tiles of 256 rows over at least 2048 keys, whose rows alone would
+ * leave CUs idle, split each query tile's keys over workgroups the same
+ * way (split-KV prefill).  Everything else takes the tiled prefill
+ * kernels.
+ * Memory: the tiled prefill kernels allocate nothing.  The split-key decode
+ * path and the split-KV prefill need a scratch array of partial states
+ * (FP32, (D + 2) floats per query row and split), taken stream-ordered
+ * with hipMallocAsync / hipFreeAsync on `stream`; under HIP graph capture
+ * those become the graph's own allocation nodes.  Callers that cannot
+ * allocate at all use attn_decode_paged_noalloc.
  */
 ATTN_API int attn_fwd(const void* Q, const void* K, const void* V, void* out,
              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,

@@ -62,7 +62,8 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
                   int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
                   int dtype, float* m_out, float* l_out, void* stream,
                   const uint32_t* mask = nullptr, int64_t mask_sb = 0, int64_t mask_sh = 0,
-                  int64_t window = 0, const attn::Problem* dropout = nullptr) {
+                  int64_t window = 0, const attn::Problem* dropout = nullptr,
+                  bool tiled_only = false) {
   g_last_error[0] = '\0';
   if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16)
     return fail(ATTN_E_INVALID, "dtype %d is not ATTN_F32, ATTN_F16 or ATTN_BF16", dtype);
@@ -147,7 +148,10 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
     e = attn::launch_fill_empty(p);
     return e == hipSuccess ? ATTN_OK : hip_fail(e, "fill kernel launch");
   }
-  if (attn::decode_route(p) && !mask && window == 0 && !dropout) {
+  // The masked and dropout entry points always take the tiled kernels (and
+  // so allocate nothing).
+  const bool plain = !tiled_only && !mask && window == 0 && !dropout;
+  if (plain && attn::decode_route(p)) {
     const attn::DecodePlan plan = attn::plan_decode(p);
     keep_pool_memory();
     void* scratch = nullptr;
@@ -157,6 +161,21 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
     const hipError_t ef = hipFreeAsync(scratch, p.stream);
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
     if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of decode scratch");
+    return ATTN_OK;
+  }
+  attn::SplitKvPlan sk;
+  if (plain && dtype != ATTN_F32 && attn::plan_prefill_splitkv(p, &sk)) {
+    keep_pool_memory();
+    void* scratch = nullptr;
+    e = hipMallocAsync(&scratch, sk.scratch_bytes, p.stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of split-key scratch");
+    p.part = static_cast<float*>(scratch);
+    p.splits = sk.splits;
+    p.split_tiles = sk.split_tiles;
+    e = attn::launch_prefill_splitkv(p);
+    const hipError_t ef = hipFreeAsync(scratch, p.stream);
+    if (e != hipSuccess) return hip_fail(e, "split-key prefill launch");
+    if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of split-key scratch");
     return ATTN_OK;
   }
   e = dtype == ATTN_F32 ? attn::launch_prefill_f32(p) : attn::launch_prefill_mfma(p);
@@ -345,7 +364,7 @@ int attn_fwd_masked(const void* Q, const void* K, const void* V, void* out, cons
                     int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, int64_t window,
                     float scale, int dtype, float* m_out, float* l_out, void* stream) {
   return run_attention(Q, K, V, out, B, H, Hkv, Nq, Nk, D, causal, scale, dtype, m_out, l_out,
-                       stream, mask, mask_stride_b, mask_stride_h, window);
+                       stream, mask, mask_stride_b, mask_stride_h, window, nullptr, true);
 }
 
 int attn_fwd_dropout(const void* Q, const void* K, const void* V, void* out, int64_t B, int64_t H,

@@ -47,10 +47,26 @@ struct Problem {
   bool dropout = false;
   uint64_t seed = 0, offset = 0;
   uint32_t drop_t = 0;
+  // Keys split over workgroups (launch_prefill_splitkv): `splits` splits of
+  // `split_tiles` 64-key tiles; FP32 partial states [B*H*Nq][splits][D + 2]
+  // in `part`.
+  float* part = nullptr;
+  int64_t splits = 0, split_tiles = 0;
 };
 
 // Streaming prefill on bf16/f16 matrix cores (prefill_mfma.hip).
 hipError_t launch_prefill_mfma(const Problem& p);
+// Plain bf16/f16 prefill with the keys of each query tile split over
+// workgroups, for few long rows (prefill_mfma.hip): whether to take it, and
+// its splits; then the tiled kernel writes partial states to p.part and the
+// decode path's combine kernel folds them, on p.stream.
+struct SplitKvPlan {
+  int64_t splits;
+  int64_t split_tiles;
+  size_t scratch_bytes;
+};
+bool plan_prefill_splitkv(const Problem& p, SplitKvPlan* plan);
+hipError_t launch_prefill_splitkv(const Problem& p);
 // Streaming prefill for FP32 inputs on the vector ALUs (prefill_f32.hip).
 hipError_t launch_prefill_f32(const Problem& p);
 
@@ -69,6 +85,9 @@ hipError_t launch_decode(const Problem& p, const DecodePlan& plan, float* scratc
 // Partial states of the split-key decode for grouped K/V heads on the matrix
 // cores (decode_gqa.hip); plan from plan_decode.
 hipError_t launch_decode_gqa_partial(const Problem& p, const DecodePlan& plan, float* scratch);
+// The combine kernel alone: folds `splits` partial states per row of
+// `scratch` ([B*H*Nq][splits][D + 2]) into out and (m, l).
+hipError_t launch_combine(const Problem& p, int splits, float* scratch);
 
 // Nk == 0: out = 0, (m, l) = (-inf, 0) (misc.hip).
 hipError_t launch_fill_empty(const Problem& p);

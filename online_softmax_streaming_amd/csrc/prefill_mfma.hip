@@ -89,12 +89,20 @@ struct PrefillArgs {
   uint64_t seed, offset;
   uint32_t drop_t;
   float keep_gain;
+  // Split-key mode (SPLITKV kernels only, batched layout): work item (head,
+  // query tile, split s) covers key tiles [s * kpt, (s + 1) * kpt) and writes
+  // each row's state (m, l, a[D]) to part[row][s], FP32, base 2, l and a
+  // relative to the exact maximum m, for the decode path's combine kernel.
+  float* part;
+  int S;    // splits per row
+  int kpt;  // key tiles per split
 };
 
 // Kernel modes: batched [B, H, N, D]; packed variable-length sequences;
 // batched with an arbitrary mask and/or a sliding window; batched with
-// dropout on the probabilities.
-enum : int { kModeBatched = 0, kModeVarlen = 1, kModeMasked = 2, kModeDropout = 3 };
+// dropout on the probabilities; batched with the keys split over
+// workgroups (partial states to scratch).
+enum : int { kModeBatched = 0, kModeVarlen = 1, kModeMasked = 2, kModeDropout = 3, kModeSplitKv = 4 };
 
 constexpr int kBN = 64;              // keys per tile
 // LDS operand reads in flight ahead of the MFMA that uses them.
@@ -119,6 +127,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
   constexpr bool VARLEN = MODE == kModeVarlen;
   constexpr bool MASKED = MODE == kModeMasked;
   constexpr bool DROPOUT = MODE == kModeDropout;
+  constexpr bool SPLITKV = MODE == kModeSplitKv;
   typedef typename Mfma<T>::vec8 vec8;
   typedef typename Mfma<T>::vec4 vec4;
   typedef typename Mfma<T>::vec2 vec2;
@@ -224,9 +233,12 @@ void prefill_mfma_kernel(PrefillArgs a) {
     kbase = (int64_t)(bh / a.group) * Nk * D;
     stat0 = (int64_t)bh * Nq;
   }
-  const int npass = CAUSAL && nqt - 1 - rr != rr ? 2 : 1;
+  // Split-key mode: one query tile per work item (no causal pairing) and
+  // split sp of its keys.
+  const int sp = SPLITKV ? rr % a.S : 0;
+  const int npass = !SPLITKV && CAUSAL && nqt - 1 - rr != rr ? 2 : 1;
   for (int pass = 0; pass < npass; ++pass) {
-    const int qt = CAUSAL ? (pass == 0 ? nqt - 1 - rr : rr) : rr;
+    const int qt = SPLITKV ? rr / a.S : CAUSAL ? (pass == 0 ? nqt - 1 - rr : rr) : rr;
 
     const int off = Nk - Nq;
     const T* __restrict__ Qh = static_cast<const T*>(a.q) + qbase;
@@ -264,8 +276,9 @@ void prefill_mfma_kernel(PrefillArgs a) {
     int kend = Nk;
     if (CAUSAL) kend = min(Nk, min(i0 + BM, Nq) + off);
     const int win = MASKED ? a.window : 0;
-    const int t_first = win > 0 ? max(0, i0 + off - win + 1) / BN : 0;
-    const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+    const int t_first = SPLITKV ? sp * a.kpt : win > 0 ? max(0, i0 + off - win + 1) / BN : 0;
+    const int ntiles = SPLITKV ? min(kend > 0 ? (kend + BN - 1) / BN : 0, (sp + 1) * a.kpt)
+                               : kend > 0 ? (kend + BN - 1) / BN : 0;
 
     // Buffer resources over this head's K and V: offsets at or past Nk rows
     // are out of range and read as zero (rows are 2*sk bytes apart; the
@@ -690,7 +703,32 @@ void prefill_mfma_kernel(PrefillArgs a) {
 
     // Epilogue: join the two half-wave sums, normalise, one cast, store.
     const float l_tot = half_sum(l_run);
-    if (qrow >= 0 && qrow < Nq) {
+    if (SPLITKV) {
+      // The split's state, relative to the exact maximum (all zero, m = -inf,
+      // for a row that sees no key of the split).
+      if (qrow >= 0 && qrow < Nq) {
+        const float to_true = m_true == kNegInf ? 0.f : exp2_hw(m_run - m_true);
+        float* prow = a.part + ((stat0 + qrow) * a.S + sp) * (D + 2);
+  #pragma unroll
+        for (int n = 0; n < NB; ++n) {
+  #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = n * 32 + g * 8 + h32 * 4;
+            if (d0 < D) {
+              // 8-byte aligned: (D + 2) and 2 + d0 are even.
+              *reinterpret_cast<f32x2*>(prow + 2 + d0) =
+                  f32x2{acc[n][g * 4] * to_true, acc[n][g * 4 + 1] * to_true};
+              *reinterpret_cast<f32x2*>(prow + 4 + d0) =
+                  f32x2{acc[n][g * 4 + 2] * to_true, acc[n][g * 4 + 3] * to_true};
+            }
+          }
+        }
+        if (h32 == 0) {
+          prow[0] = m_true;
+          prow[1] = l_tot * to_true;
+        }
+      }
+    } else if (qrow >= 0 && qrow < Nq) {
       float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       if (DROPOUT) inv *= a.keep_gain;
       T* orow = Oh + (int64_t)qrow * sq;
@@ -748,7 +786,10 @@ hipError_t launch_typed(const Problem& p) {
   a.offset = p.offset;
   a.drop_t = p.drop_t;
   a.keep_gain = (float)(65536.0 / (65536.0 - (double)p.drop_t));
-  a.nwork = CAUSAL ? (a.nqt + 1) / 2 : a.nqt;
+  a.part = p.part;
+  a.S = (int)p.splits;
+  a.kpt = (int)p.split_tiles;
+  a.nwork = MODE == kModeSplitKv ? a.nqt * a.S : CAUSAL ? (a.nqt + 1) / 2 : a.nqt;
   const int64_t total = p.B * p.H * a.nwork;
   a.total = (int)total;
   const int64_t grid = (total + 7) / 8 * 8;
@@ -774,6 +815,15 @@ constexpr int kWaves = ATTN_PREFILL_WAVES;
 // against 27.0 us).
 template <int D>
 constexpr int64_t kSmallGridWgs = D > 64 ? 63 : 64;
+#ifndef SPLITKV_MAX_WQ
+#define SPLITKV_MAX_WQ 64
+#endif
+#ifndef SPLITKV_MIN_TILES
+#define SPLITKV_MIN_TILES 16
+#endif
+#ifndef SPLITKV_TARGET_WGS
+#define SPLITKV_TARGET_WGS 256
+#endif
 constexpr int64_t kNumCUs = 256;
 
 // Every layout of one workgroup size.
@@ -836,7 +886,80 @@ hipError_t launch_t(const Problem& p) {
   }
 }
 
+template <typename T, int D>
+hipError_t launch_splitkv_d(const Problem& p) {
+  const hipError_t e = p.causal ? launch_typed<T, D, kWaves, true, kModeSplitKv>(p)
+                                : launch_typed<T, D, kWaves, false, kModeSplitKv>(p);
+  if (e != hipSuccess) return e;
+  return launch_combine(p, (int)p.splits, p.part);
+}
+
+template <typename T>
+hipError_t launch_splitkv_t(const Problem& p) {
+  switch (p.D) {
+    case 16: return launch_splitkv_d<T, 16>(p);
+    case 32: return launch_splitkv_d<T, 32>(p);
+    case 64: return launch_splitkv_d<T, 64>(p);
+    case 128: return launch_splitkv_d<T, 128>(p);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+bool plan_prefill_splitkv(const Problem& p, SplitKvPlan* plan) {
+  // Query tiles of the eight-wave kernel (no causal pairing here) and key
+  // tiles: few query tiles over many keys cannot fill the GPU by rows, so
+  // their keys are split over workgroups, each split at least
+  // SPLITKV_MIN_TILES key tiles long, for about one workgroup per CU.
+  const int64_t nqt = (p.Nq + 32 * kWaves - 1) / (32 * kWaves);
+  const int64_t wq = p.B * p.H * nqt;
+  const int64_t kt = (p.Nk + kBN - 1) / kBN;
+  if (wq > SPLITKV_MAX_WQ || kt < 2 * SPLITKV_MIN_TILES) return false;
+  int64_t S = (SPLITKV_TARGET_WGS + wq - 1) / wq;
+  if (S > kt / SPLITKV_MIN_TILES) S = kt / SPLITKV_MIN_TILES;
+  if (S < 2) return false;
+  const int64_t kpt = (kt + S - 1) / S;
+  S = (kt + kpt - 1) / kpt;
+  // Rows x keys streamed by the busiest CU, here (padding rows of the
+  // 256-row tiles included) and on the route launch_prefill_mfma takes
+  // otherwise: the key-split kernel, one four-wave workgroup per 32-row
+  // block over all keys, or at D = 128 with 64 eight-wave workgroups,
+  // four-wave tiled workgroups of 128 rows (two tiles each when causal).
+  // Split keys when that load is lower; at D = 128 also when it is equal,
+  // where the tiled kernel's two waves per SIMD beat the key-split
+  // kernel's one (B1 H32 Nq512 Nk8192 causal 125 -> 88 us, B1 H8 Nq1024
+  // Nk8192 65 -> 57 us); at D <= 64 an equal load goes either way (B1 H4
+  // Nq256 Nk8192 causal 34 -> 29 us, B1 H8 Nq1024 Nk8192 34 -> 44 us) and
+  // stays with the key-split kernel.  Lower loads: B1 H8 Nq512 Nk16384 D128 causal 117 -> 55 us,
+  // B1 H1 Nq512 Nk65536 D64 causal 227 -> 49 us, B1 H4 Nq512 Nk32768 D16
+  // 78 -> 34 us; higher ones lose (B4 H8 Nq256 Nk4096 D128 causal 37 ->
+  // 44 us).
+  auto per_cu = [](int64_t wgs) { return (wgs + kNumCUs - 1) / kNumCUs; };
+  const int64_t bh = p.B * p.H;
+  const int64_t w8 = bh * (p.causal ? (nqt + 1) / 2 : nqt);
+  const int64_t small = p.D > 64 ? kSmallGridWgs<128> : kSmallGridWgs<64>;
+  int64_t other;
+  if (w8 <= small) {
+    other = per_cu(bh * ((p.Nq + 31) / 32)) * 32 * p.Nk;
+  } else {
+    const int64_t nqt4 = (p.Nq + 127) / 128;
+    const bool pair = p.causal && nqt4 > 1;
+    other = per_cu(bh * (p.causal ? (nqt4 + 1) / 2 : nqt4)) * (pair ? 256 : 128) * p.Nk;
+  }
+  const int64_t mine = per_cu(wq * S) * 32 * kWaves * kpt * kBN;
+  if (mine > other || (mine == other && p.D <= 64)) return false;
+  plan->splits = S;
+  plan->split_tiles = kpt;
+  plan->scratch_bytes = (size_t)(p.B * p.H * p.Nq) * (size_t)S * (size_t)(p.D + 2) * sizeof(float);
+  return true;
+}
+
+hipError_t launch_prefill_splitkv(const Problem& p) {
+  if (p.dtype == DType::BF16) return launch_splitkv_t<__bf16>(p);
+  if (p.dtype == DType::F16) return launch_splitkv_t<_Float16>(p);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_prefill_mfma(const Problem& p) {
   if (p.dtype == DType::BF16) return launch_t<__bf16>(p);

@@ -463,3 +463,29 @@ def test_fp32_small_grid_split_and_default_split(causal, nq, nk, d):
     for rep in (0, 137, 255):
         _compare_full(q, k, v, causal, scale, wide[rep:rep + 1], TOL["f32"], wm[rep:rep + 1],
                       wl[rep:rep + 1])
+
+
+@pytest.mark.parametrize("b,h,nq,nk,d,causal,dtype", [
+    # Few 256-row query tiles over many keys: the keys of each tile are split
+    # over workgroups and the partial states combined (4 to 64 splits; ragged
+    # query tiles, a ragged last split and key tile).
+    (1, 4, 256, 8192, 128, True, "bf16"), (1, 1, 512, 65536, 128, True, "bf16"),
+    (1, 1, 1000, 20000, 64, False, "f16"), (2, 1, 300, 12000, 128, False, "bf16"),
+    (1, 2, 256, 16384, 32, True, "bf16"), (1, 1, 512, 32768, 16, False, "f16"),
+    # Causal with Nq = Nk: splits past the diagonal see no key of their rows.
+    (1, 1, 8192, 8192, 128, True, "bf16"),
+    # More rows than keys, causal: the first Nq - Nk rows see no key at all.
+    (1, 1, 8200, 8192, 128, True, "bf16")])
+def test_split_kv_route(b, h, nq, nk, d, causal, dtype):
+    # Every head compared in full, row states included, and the result
+    # repeatable bit for bit.
+    _say(f"split-kv B={b} H={h} Nq={nq} Nk={nk} D={d} causal={causal} {dtype}")
+    q, k, v = random_qkv(b, h, nq, nk, d, dtype, seed=nq + nk + d, device=DEV, k_ramp=0.002)
+    scale = default_scale(d)
+    out, m, l = attn_fwd_stats(q, k, v, causal=causal, scale=scale)
+    again = attn_fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(again, out), "the split-kv path is not deterministic"
+    err = _compare_full(q, k, v, causal, scale, out, TOL[dtype], m, l)
+    _record(f"split-kv B={b} H={h} Nq={nq} Nk={nk} D={d} causal={causal} {dtype}", err,
+            TOL[dtype])

@@ -84,6 +84,14 @@ def test_decode_route_mid_rows(lib, dtype, causal, h, hkv, nq, nk, d):
     test_parity(lib, dtype, causal, h, hkv, nq, nk, d)
 
 
+@pytest.mark.parametrize("dtype,causal,h,hkv,nq,nk,d", [
+    ("bf16", True, 8, 2, 256, 8192, 128), ("f16", False, 4, 1, 300, 12000, 64)])
+def test_split_kv_grouped(lib, dtype, causal, h, hkv, nq, nk, d):
+    # Few query tiles over many keys with grouped K/V heads: each tile's keys
+    # split over workgroups (8 and 11 splits), partial states combined.
+    test_parity(lib, dtype, causal, h, hkv, nq, nk, d)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("nq", [1, 300])
 def test_equals_mha_on_repeated_kv(lib, dtype, nq):

@@ -42,6 +42,10 @@ def _capture(fn):
     ("bf16", 128, True, 300, 300),
     ("f16", 64, False, 77, 533),
     ("f32", 64, True, 130, 130),
+    # Paths with stream-ordered scratch (allocation nodes in the graph): the
+    # split-KV prefill (8 key splits) and the split-key decode.
+    ("bf16", 128, True, 256, 8192),
+    ("f16", 64, False, 4, 3000),
 ])
 def test_replay_matches_eager(dtype, d, causal, nq, nk):
     q, k, v = random_qkv(2, 3, nq, nk, d, dtype, seed=nq + nk, device="cuda")

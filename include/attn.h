@@ -98,10 +98,17 @@ extern "C" {
  * kernels.
  * Memory: the tiled prefill kernels allocate nothing.  The split-key decode
  * path and the split-KV prefill need a scratch array of partial states
- * (FP32, (D + 2) floats per query row and split), taken stream-ordered
- * with hipMallocAsync / hipFreeAsync on `stream`; under HIP graph capture
- * those become the graph's own allocation nodes.  Callers that cannot
- * allocate at all use attn_decode_paged_noalloc.
+ * (FP32, (D + 2) floats per query row and split).  The library keeps one
+ * such buffer per (device, stream), taken with hipMallocAsync on `stream`,
+ * grown on demand in 1 MiB steps and held until the process ends; calls on
+ * one stream reuse it in stream order, and every call that takes scratch
+ * (this one, attn_bwd, attn_decode_paged, softmax_rows) shares it.  A
+ * stream on which such a call may still run must be synchronised before it
+ * is destroyed (a new stream may receive its handle, and with it the
+ * buffer).
+ * Under HIP graph capture each call instead takes its own hipMallocAsync /
+ * hipFreeAsync pair, which become the graph's allocation nodes.  Callers
+ * that cannot allocate at all use attn_decode_paged_noalloc.
  */
 ATTN_API int attn_fwd(const void* Q, const void* K, const void* V, void* out,
              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
@@ -175,8 +182,7 @@ ATTN_API int attn_fwd_gqa(const void* Q, const void* K, const void* V, void* out
  *                   (D in {16, 32, 64, 128}); additionally B*Hkv*Nk < 2^31.
  *                   Nq == 0 writes dK = dV = 0; Nk == 0 writes dQ = 0.
  * Memory: a scratch array of 8 * B*H*Nq bytes (per row the base-2 lse and
- * Delta), taken with hipMallocAsync and released with hipFreeAsync on
- * `stream`.  Two kernels are queued: dQ (which also fills the scratch),
+ * Delta), the per-stream scratch described under attn_fwd.  Two kernels are queued: dQ (which also fills the scratch),
  * then dK and dV.
  * Returns ATTN_OK once queued, else the status codes of attn_fwd.
  */
@@ -321,8 +327,8 @@ ATTN_API int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* 
  *            max_pages * page_size < 2^31, B * H * Nq < 2^31.
  *   causal   0 or 1; window >= 0 (0 = none; > 0 needs causal == 1).
  *   D, scale, dtype, stream: as attn_fwd.  B, H or Nq == 0 is a no-op.
- * Memory: partial states of the key splits in a scratch array taken with
- * hipMallocAsync / hipFreeAsync on `stream`.
+ * Memory: partial states of the key splits in the per-stream scratch
+ * described under attn_fwd.
  * Returns ATTN_OK once queued; ATTN_E_INVALID / ATTN_E_UNSUPPORTED /
  * ATTN_E_HIP as attn_fwd.
  */
@@ -424,8 +430,8 @@ ATTN_API int online_merge_batch(const float* m1, const float* l1,
  *       are all -inf is written as zeros.  NaN and +inf are outside the
  *       contract.
  * Scratch: FP32 (m, l) per chunk and per row, 8 * M * (T + 1) bytes with
- *       T = ceil(N / chunk), taken with hipMallocAsync and released with
- *       hipFreeAsync on `stream`.
+ *       T = ceil(N / chunk), in the per-stream scratch described under
+ *       attn_fwd.
  * Returns ATTN_OK once queued; ATTN_E_INVALID for bad arguments,
  * ATTN_E_UNSUPPORTED when M * T reaches 2^31, ATTN_E_HIP if a launch or
  * the scratch allocation fails.

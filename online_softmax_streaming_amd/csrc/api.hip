@@ -9,7 +9,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "../../include/attn.h"
 #include "attn_kernels.h"
@@ -57,6 +59,95 @@ void keep_pool_memory() {
   }
   done[dev] = true;
 }
+
+// Scratch of the paths that keep partial states (split-key decode, split-KV
+// prefill, backward, wide-row softmax).  A stream-ordered hipMallocAsync /
+// hipFreeAsync pair per call left the GPU idle ~5.6 us before the next
+// call's first kernel, so outside graph capture each (device, stream) keeps
+// one buffer, grown on demand (in 1 MiB steps) and never shrunk, until the
+// process ends.  Work on one stream runs in issue order, so a call's kernels
+// use the buffer only after the previous call's kernels on that stream; the
+// lock is held from the lookup to the last launch, so another host thread
+// cannot grow (free) the buffer between them.  Streams are keyed by handle:
+// a stream destroyed while such a call may still run on it must be
+// synchronised first, as a new stream may take over its handle (and
+// buffer).  Under graph capture each call takes its own hipMallocAsync /
+// hipFreeAsync pair, which capture records as the graph's allocation nodes.
+constexpr size_t kScratchGrain = size_t(1) << 20;
+
+struct StreamScratch {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+
+std::mutex g_scratch_mu;
+
+std::map<std::pair<int, uintptr_t>, StreamScratch>& scratch_map() {
+  static std::map<std::pair<int, uintptr_t>, StreamScratch> m;
+  return m;
+}
+
+class ScratchLease {
+ public:
+  ScratchLease() = default;
+  ScratchLease(const ScratchLease&) = delete;
+  ScratchLease& operator=(const ScratchLease&) = delete;
+  ~ScratchLease() { (void)release(); }
+
+  // `bytes` of device scratch for work queued on `s` until release().
+  hipError_t acquire(hipStream_t s, size_t bytes) {
+    s_ = s;
+    if (bytes == 0) return hipSuccess;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(s, &cs);
+    if (e != hipSuccess) return e;
+    keep_pool_memory();
+    if (cs != hipStreamCaptureStatusNone) {
+      owned_ = true;
+      return hipMallocAsync(&ptr_, bytes, s);
+    }
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    lock_ = std::unique_lock<std::mutex>(g_scratch_mu);
+    StreamScratch& b = scratch_map()[std::make_pair(dev, reinterpret_cast<uintptr_t>(s))];
+    if (b.bytes < bytes) {
+      if (b.ptr) {
+        e = hipFreeAsync(b.ptr, s);
+        b.ptr = nullptr;
+        b.bytes = 0;
+        if (e != hipSuccess) return e;
+      }
+      const size_t want = (bytes + kScratchGrain - 1) / kScratchGrain * kScratchGrain;
+      e = hipMallocAsync(&b.ptr, want, s);
+      if (e != hipSuccess) {
+        b.ptr = nullptr;
+        return e;
+      }
+      b.bytes = want;
+    }
+    ptr_ = b.ptr;
+    return hipSuccess;
+  }
+
+  float* ptr() const { return static_cast<float*>(ptr_); }
+
+  // After the last launch that uses the scratch.
+  hipError_t release() {
+    hipError_t e = hipSuccess;
+    if (owned_ && ptr_) e = hipFreeAsync(ptr_, s_);
+    owned_ = false;
+    ptr_ = nullptr;
+    if (lock_.owns_lock()) lock_.unlock();
+    return e;
+  }
+
+ private:
+  std::unique_lock<std::mutex> lock_;
+  void* ptr_ = nullptr;
+  hipStream_t s_ = nullptr;
+  bool owned_ = false;
+};
 
 int run_attention(const void* Q, const void* K, const void* V, void* out, int64_t B, int64_t H,
                   int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
@@ -153,27 +244,25 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
   const bool plain = !tiled_only && !mask && window == 0 && !dropout;
   if (plain && attn::decode_route(p)) {
     const attn::DecodePlan plan = attn::plan_decode(p);
-    keep_pool_memory();
-    void* scratch = nullptr;
-    e = hipMallocAsync(&scratch, plan.scratch_bytes, p.stream);
-    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of decode scratch");
-    e = attn::launch_decode(p, plan, static_cast<float*>(scratch));
-    const hipError_t ef = hipFreeAsync(scratch, p.stream);
+    ScratchLease scratch;
+    e = scratch.acquire(p.stream, plan.scratch_bytes);
+    if (e != hipSuccess) return hip_fail(e, "decode scratch allocation");
+    e = attn::launch_decode(p, plan, scratch.ptr());
+    const hipError_t ef = scratch.release();
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
     if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of decode scratch");
     return ATTN_OK;
   }
   attn::SplitKvPlan sk;
   if (plain && dtype != ATTN_F32 && attn::plan_prefill_splitkv(p, &sk)) {
-    keep_pool_memory();
-    void* scratch = nullptr;
-    e = hipMallocAsync(&scratch, sk.scratch_bytes, p.stream);
-    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of split-key scratch");
-    p.part = static_cast<float*>(scratch);
+    ScratchLease scratch;
+    e = scratch.acquire(p.stream, sk.scratch_bytes);
+    if (e != hipSuccess) return hip_fail(e, "split-key scratch allocation");
+    p.part = scratch.ptr();
     p.splits = sk.splits;
     p.split_tiles = sk.split_tiles;
     e = attn::launch_prefill_splitkv(p);
-    const hipError_t ef = hipFreeAsync(scratch, p.stream);
+    const hipError_t ef = scratch.release();
     if (e != hipSuccess) return hip_fail(e, "split-key prefill launch");
     if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of split-key scratch");
     return ATTN_OK;
@@ -324,12 +413,11 @@ int run_paged(const void* Q, const void* K_cache, const void* V_cache,
     return e == hipSuccess ? ATTN_OK : hip_fail(e, "paged decode kernel launch");
   }
   const attn::DecodePlan plan = attn::plan_decode(p);
-  keep_pool_memory();
-  void* scratch = nullptr;
-  hipError_t e = hipMallocAsync(&scratch, plan.scratch_bytes, p.stream);
-  if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of decode scratch");
-  e = attn::launch_decode(p, plan, static_cast<float*>(scratch));
-  const hipError_t ef = hipFreeAsync(scratch, p.stream);
+  ScratchLease scratch;
+  hipError_t e = scratch.acquire(p.stream, plan.scratch_bytes);
+  if (e != hipSuccess) return hip_fail(e, "decode scratch allocation");
+  e = attn::launch_decode(p, plan, scratch.ptr());
+  const hipError_t ef = scratch.release();
   if (e != hipSuccess) return hip_fail(e, "paged decode kernel launch");
   if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of decode scratch");
   return ATTN_OK;
@@ -463,16 +551,12 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
   p.stream = static_cast<hipStream_t>(stream);
 
   const size_t sb = attn::bwd_scratch_bytes(p);
-  void* scratch = nullptr;
-  hipError_t e;
-  if (sb > 0) {
-    keep_pool_memory();
-    e = hipMallocAsync(&scratch, sb, p.stream);
-    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of backward scratch");
-  }
-  e = dtype == ATTN_F32 ? attn::launch_bwd_f32(p, static_cast<float*>(scratch))
-                        : attn::launch_bwd_mfma(p, static_cast<float*>(scratch));
-  const hipError_t ef = scratch ? hipFreeAsync(scratch, p.stream) : hipSuccess;
+  ScratchLease scratch;
+  hipError_t e = scratch.acquire(p.stream, sb);
+  if (e != hipSuccess) return hip_fail(e, "backward scratch allocation");
+  e = dtype == ATTN_F32 ? attn::launch_bwd_f32(p, scratch.ptr())
+                        : attn::launch_bwd_mfma(p, scratch.ptr());
+  const hipError_t ef = scratch.release();
   if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of backward scratch");
   return ATTN_OK;
@@ -639,13 +723,12 @@ int softmax_rows(const void* x, void* y, int64_t M, int64_t N, int64_t chunk, in
   if (M > kI32Max || T > kI32Max / M)
     return fail(ATTN_E_UNSUPPORTED, "softmax_rows: M * ceil(N / chunk) must be < 2^31");
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  keep_pool_memory();
-  void* scratch = nullptr;
-  hipError_t e = hipMallocAsync(&scratch, (size_t)attn::softmax_scratch_bytes(M, N, c), s);
-  if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of softmax scratch");
+  ScratchLease scratch;
+  hipError_t e = scratch.acquire(s, (size_t)attn::softmax_scratch_bytes(M, N, c));
+  if (e != hipSuccess) return hip_fail(e, "softmax scratch allocation");
   e = attn::launch_softmax_split(x, y, M, N, (int)c, static_cast<attn::DType>(dtype),
-                                 static_cast<float*>(scratch), s);
-  const hipError_t ef = hipFreeAsync(scratch, s);
+                                 scratch.ptr(), s);
+  const hipError_t ef = scratch.release();
   if (e != hipSuccess) return hip_fail(e, "softmax kernel launch");
   if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of softmax scratch");
   return ATTN_OK;

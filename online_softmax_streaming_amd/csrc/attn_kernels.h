@@ -48,8 +48,8 @@ struct Problem {
   uint64_t seed = 0, offset = 0;
   uint32_t drop_t = 0;
   // Keys split over workgroups (launch_prefill_splitkv): `splits` splits of
-  // `split_tiles` 64-key tiles; FP32 partial states [B*H*Nq][splits][D + 2]
-  // in `part`.
+  // `split_tiles` 64-key tiles; FP32 partial states in `part`: a[D] as
+  // [B*H*Nq][splits][D], then (m, l) as [B*H*Nq][splits][2].
   float* part = nullptr;
   int64_t splits = 0, split_tiles = 0;
 };
@@ -58,8 +58,8 @@ struct Problem {
 hipError_t launch_prefill_mfma(const Problem& p);
 // Plain bf16/f16 prefill with the keys of each query tile split over
 // workgroups, for few long rows (prefill_mfma.hip): whether to take it, and
-// its splits; then the tiled kernel writes partial states to p.part and the
-// decode path's combine kernel folds them, on p.stream.
+// its splits; then the tiled kernel writes partial states to p.part and a
+// combine kernel folds them, on p.stream.
 struct SplitKvPlan {
   int64_t splits;
   int64_t split_tiles;
@@ -85,9 +85,6 @@ hipError_t launch_decode(const Problem& p, const DecodePlan& plan, float* scratc
 // Partial states of the split-key decode for grouped K/V heads on the matrix
 // cores (decode_gqa.hip); plan from plan_decode.
 hipError_t launch_decode_gqa_partial(const Problem& p, const DecodePlan& plan, float* scratch);
-// The combine kernel alone: folds `splits` partial states per row of
-// `scratch` ([B*H*Nq][splits][D + 2]) into out and (m, l).
-hipError_t launch_combine(const Problem& p, int splits, float* scratch);
 
 // Nk == 0: out = 0, (m, l) = (-inf, 0) (misc.hip).
 hipError_t launch_fill_empty(const Problem& p);

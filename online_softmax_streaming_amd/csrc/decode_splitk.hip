@@ -280,30 +280,6 @@ hipError_t launch_typed(const Problem& p, const DecodePlan& plan, float* scratch
 }
 
 template <typename T, int D>
-hipError_t launch_combine_d(const Problem& p, int splits, float* scratch) {
-  DecodeArgs a{};
-  a.o = p.o;
-  a.m_out = p.m_out;
-  a.l_out = p.l_out;
-  a.part = scratch;
-  a.S = splits;
-  const int64_t rows = p.B * p.H * p.Nq;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)rows), dim3(128), 0, p.stream, a);
-  return hipGetLastError();
-}
-
-template <typename T>
-hipError_t launch_combine_t(const Problem& p, int splits, float* scratch) {
-  switch (p.D) {
-    case 16: return launch_combine_d<T, 16>(p, splits, scratch);
-    case 32: return launch_combine_d<T, 32>(p, splits, scratch);
-    case 64: return launch_combine_d<T, 64>(p, splits, scratch);
-    case 128: return launch_combine_d<T, 128>(p, splits, scratch);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <typename T, int D>
 hipError_t launch_d(const Problem& p, const DecodePlan& plan, float* scratch) {
   if (p.table)
     return p.causal ? launch_typed<T, D, true, true>(p, plan, scratch)
@@ -419,12 +395,6 @@ DecodePlan plan_decode(const Problem& p, int64_t max_splits) {
   plan.keys_per_split = (int)kps;
   plan.scratch_bytes = (size_t)rows * (size_t)splits * (size_t)(p.D + 2) * sizeof(float);
   return plan;
-}
-
-hipError_t launch_combine(const Problem& p, int splits, float* scratch) {
-  if (p.dtype == DType::BF16) return launch_combine_t<__bf16>(p, splits, scratch);
-  if (p.dtype == DType::F16) return launch_combine_t<_Float16>(p, splits, scratch);
-  return launch_combine_t<float>(p, splits, scratch);
 }
 
 hipError_t launch_decode(const Problem& p, const DecodePlan& plan, float* scratch) {

@@ -91,9 +91,10 @@ struct PrefillArgs {
   float keep_gain;
   // Split-key mode (SPLITKV kernels only, batched layout): work item (head,
   // query tile, split s) covers key tiles [s * kpt, (s + 1) * kpt) and writes
-  // each row's state (m, l, a[D]) to part[row][s], FP32, base 2, l and a
-  // relative to the exact maximum m, for the decode path's combine kernel.
+  // each row's state, FP32, base 2, l and a relative to the exact maximum m:
+  // a[D] to part[row][s][.], (m, l) to part_ml[row][s][.].
   float* part;
+  float* part_ml;
   int S;    // splits per row
   int kpt;  // key tiles per split
 };
@@ -704,29 +705,25 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // Epilogue: join the two half-wave sums, normalise, one cast, store.
     const float l_tot = half_sum(l_run);
     if (SPLITKV) {
-      // The split's state, relative to the exact maximum (all zero, m = -inf,
-      // for a row that sees no key of the split).
+      // The split's state, relative to the exact maximum (a = 0, l = 0,
+      // m = -inf for a row that sees no key of the split).
       if (qrow >= 0 && qrow < Nq) {
         const float to_true = m_true == kNegInf ? 0.f : exp2_hw(m_run - m_true);
-        float* prow = a.part + ((stat0 + qrow) * a.S + sp) * (D + 2);
+        const int64_t st = (stat0 + qrow) * a.S + sp;
+        float* pa = a.part + st * D;
   #pragma unroll
         for (int n = 0; n < NB; ++n) {
   #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int d0 = n * 32 + g * 8 + h32 * 4;
-            if (d0 < D) {
-              // 8-byte aligned: (D + 2) and 2 + d0 are even.
-              *reinterpret_cast<f32x2*>(prow + 2 + d0) =
-                  f32x2{acc[n][g * 4] * to_true, acc[n][g * 4 + 1] * to_true};
-              *reinterpret_cast<f32x2*>(prow + 4 + d0) =
-                  f32x2{acc[n][g * 4 + 2] * to_true, acc[n][g * 4 + 3] * to_true};
-            }
+            if (d0 < D)
+              *reinterpret_cast<f32x4*>(pa + d0) =
+                  f32x4{acc[n][g * 4] * to_true, acc[n][g * 4 + 1] * to_true,
+                        acc[n][g * 4 + 2] * to_true, acc[n][g * 4 + 3] * to_true};
           }
         }
-        if (h32 == 0) {
-          prow[0] = m_true;
-          prow[1] = l_tot * to_true;
-        }
+        if (h32 == 0)
+          *reinterpret_cast<f32x2*>(a.part_ml + 2 * st) = f32x2{m_true, l_tot * to_true};
       }
     } else if (qrow >= 0 && qrow < Nq) {
       float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -787,6 +784,7 @@ hipError_t launch_typed(const Problem& p) {
   a.drop_t = p.drop_t;
   a.keep_gain = (float)(65536.0 / (65536.0 - (double)p.drop_t));
   a.part = p.part;
+  a.part_ml = p.part ? p.part + p.B * p.H * p.Nq * p.splits * D : nullptr;
   a.S = (int)p.splits;
   a.kpt = (int)p.split_tiles;
   a.nwork = MODE == kModeSplitKv ? a.nqt * a.S : CAUSAL ? (a.nqt + 1) / 2 : a.nqt;
@@ -886,12 +884,60 @@ hipError_t launch_t(const Problem& p) {
   }
 }
 
+// Folds the S split states of each row (merge A1, all splits at once: the
+// exact maximum M over the splits, then weights 2^(m_s - M)) into out and
+// (m, l).  D / 4 lanes per row, four features per lane, 16-byte loads; the
+// S partial vectors of a row are contiguous, so its loads are independent.
+constexpr int kCombineThreads = 256;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kCombineThreads) void splitkv_combine_kernel(
+    const float* __restrict__ part, const float* __restrict__ part_ml, T* __restrict__ out,
+    float* __restrict__ m_out, float* __restrict__ l_out, int rows, int S) {
+  constexpr int LPR = D / 4;
+  constexpr int RPB = kCombineThreads / LPR;
+  const int lr = threadIdx.x % LPR;
+  const int row = blockIdx.x * RPB + threadIdx.x / LPR;
+  if (row >= rows) return;
+  const f32x2* ml = reinterpret_cast<const f32x2*>(part_ml) + (int64_t)row * S;
+  float M = kNegInf;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s][0]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  if (M != kNegInf) {
+    const f32x4* pa = reinterpret_cast<const f32x4*>(part + (int64_t)row * S * D) + lr;
+  #pragma unroll 4
+    for (int s = 0; s < S; ++s) {
+      const f32x2 st = ml[s];
+      const float w = exp2_hw(st[0] - M);  // 0 for a split with no visible key
+      L += w * st[1];
+      acc += w * pa[s * LPR];
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  T o[4];
+  #pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(acc[j] * inv);
+  u32x2 bits;
+  __builtin_memcpy(&bits, o, sizeof(bits));
+  *reinterpret_cast<u32x2*>(out + (int64_t)row * D + 4 * lr) = bits;
+  if (lr == 0) {
+    if (m_out) m_out[row] = M * kLn2;
+    if (l_out) l_out[row] = L;
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_splitkv_d(const Problem& p) {
   const hipError_t e = p.causal ? launch_typed<T, D, kWaves, true, kModeSplitKv>(p)
                                 : launch_typed<T, D, kWaves, false, kModeSplitKv>(p);
   if (e != hipSuccess) return e;
-  return launch_combine(p, (int)p.splits, p.part);
+  const int64_t rows = p.B * p.H * p.Nq;
+  constexpr int RPB = kCombineThreads / (D / 4);
+  hipLaunchKernelGGL((splitkv_combine_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)),
+                     dim3(kCombineThreads), 0, p.stream, p.part, p.part + rows * p.splits * D,
+                     static_cast<T*>(p.o), p.m_out, p.l_out, (int)rows, (int)p.splits);
+  return hipGetLastError();
 }
 
 template <typename T>

@@ -95,6 +95,9 @@ WORKLOADS = {w.name: w for w in [
     Workload("ragged_b0_f16", 0, 8, 4099, 4099, 64, "f16", True, 0.02),
     Workload("long_causal_bf16", 1, 32, 16384, 16384, 128, "bf16", True),
     Workload("decode_bf16", 16, 32, 1, 32768, 128, "bf16", False),
+    # A 512-token chunk of new rows over an 8192-token context (causal, the
+    # chunk's rows are the context's last 512): few query tiles over many keys.
+    Workload("chunked_causal_bf16", 1, 32, 512, 8192, 128, "bf16", True),
 ]}
 
 

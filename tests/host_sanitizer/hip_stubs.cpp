@@ -48,6 +48,10 @@ int hipMallocAsync(void** p, size_t, void*) {
   return kNoDevice;
 }
 int hipFreeAsync(void*, void*) { return kNoDevice; }
+int hipStreamIsCapturing(void*, int* status) {
+  *status = 0;  // hipStreamCaptureStatusNone
+  return kNoDevice;
+}
 int hipDeviceGetDefaultMemPool(void** pool, int) {
   *pool = nullptr;
   return kNoDevice;

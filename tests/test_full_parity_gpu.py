@@ -70,10 +70,12 @@ def _compare_heads(w, seed, heads=None):
 
 
 @pytest.mark.parametrize("name", ["ragged_causal_f16", "ragged_noncausal_f16",
-                                  "headline_noncausal_bf16", "headline_causal_bf16"])
+                                  "headline_noncausal_bf16", "headline_causal_bf16",
+                                  "chunked_causal_bf16"])
 def test_every_head_in_full(name):
-    # Ragged fp16 (24 heads, 4099 rows with the rising key ramp) and both
-    # headline bf16 workloads (64 heads): every element of every head.
+    # Ragged fp16 (24 heads, 4099 rows with the rising key ramp), both
+    # headline bf16 workloads (64 heads) and the chunked-prefill workload (32
+    # heads, keys split over workgroups): every element of every head.
     rec = _compare_heads(WORKLOADS[name], seed=0)
     assert rec["over_tol"] == 0, rec
 

@@ -217,24 +217,57 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
   }
 }
 
+// Folds the S split states of each row into out and (m, l), merge A1 over
+// groups of up to 16 splits: a group's states are loaded at once (one round
+// of memory latency per group), then weighted by 2^(m_s - M) against the
+// exact maximum M so far, the running sums rescaled when M grows.  D / 2
+// lanes per row, two features per lane (8-byte loads: a split's a[D] starts
+// 8 bytes into its D + 2 floats).
+constexpr int kCombineThreads = 256;
+constexpr int kCombineGroup = 16;
+
 template <typename T, int D>
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
-  const int row = blockIdx.x;
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeArgs a, int rows) {
+  constexpr int LPR = D / 2;
+  constexpr int RPB = kCombineThreads / LPR;
+  const int lr = threadIdx.x % LPR;
+  const int row = blockIdx.x * RPB + threadIdx.x / LPR;
+  if (row >= rows) return;
   const float* src = a.part + (int64_t)row * a.S * (D + 2);
-  float M = kNegInf, L = 0.f, A = 0.f;
-  for (int s = 0; s < a.S; ++s) {
-    const float* st = src + (int64_t)s * (D + 2);
-    const MergeWeights w = merge_weights_log2(M, st[0]);
-    L = L * w.w1 + st[1] * w.w2;
-    if (tid < D) A = A * w.w1 + st[2 + tid] * w.w2;
-    M = w.m;
+  float M = kNegInf, L = 0.f;
+  f32x2 acc = {0.f, 0.f};
+  for (int s0 = 0; s0 < a.S; s0 += kCombineGroup) {
+    float m[kCombineGroup], l[kCombineGroup];
+    f32x2 x[kCombineGroup];
+    // Past the last split the loads repeat it (no branches between the
+    // loads) and its maximum is masked out; its weight below is 0.
+  #pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) {
+      const float* st = src + min(s0 + j, a.S - 1) * (D + 2);
+      m[j] = s0 + j < a.S ? st[0] : kNegInf;
+      l[j] = st[1];
+      x[j] = *reinterpret_cast<const f32x2*>(st + 2 + 2 * lr);
+    }
+    float mg = M;
+  #pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) mg = fmaxf(mg, m[j]);
+    if (mg == kNegInf) continue;  // no visible key in any split so far
+    const float r = exp2_hw(M - mg);  // 0 while M = -inf (L and acc are 0)
+    L *= r;
+    acc *= r;
+  #pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) {
+      const float w = exp2_hw(m[j] - mg);  // 0 for a split with no visible key
+      L += w * l[j];
+      acc += w * x[j];
+    }
+    M = mg;
   }
-  if (tid < D) {
-    const float out = L > 0.f ? A / L : 0.f;
-    static_cast<T*>(a.o)[(int64_t)row * D + tid] = from_f32<T>(out);
-  }
-  if (tid == 0) {
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  T* orow = static_cast<T*>(a.o) + (int64_t)row * D + 2 * lr;
+  orow[0] = from_f32<T>(acc[0] * inv);
+  orow[1] = from_f32<T>(acc[1] * inv);
+  if (lr == 0) {
     if (a.m_out) a.m_out[row] = M * kLn2;
     if (a.l_out) a.l_out[row] = L;
   }
@@ -275,7 +308,9 @@ hipError_t launch_typed(const Problem& p, const DecodePlan& plan, float* scratch
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)rows), dim3(128), 0, p.stream, a);
+  constexpr int RPB = kCombineThreads / (D / 2);
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)),
+                     dim3(kCombineThreads), 0, p.stream, a, (int)rows);
   return hipGetLastError();
 }
 

@@ -884,11 +884,13 @@ hipError_t launch_t(const Problem& p) {
   }
 }
 
-// Folds the S split states of each row (merge A1, all splits at once: the
-// exact maximum M over the splits, then weights 2^(m_s - M)) into out and
-// (m, l).  D / 4 lanes per row, four features per lane, 16-byte loads; the
-// S partial vectors of a row are contiguous, so its loads are independent.
+// Folds the S split states of each row into out and (m, l), merge A1 over
+// groups of up to 16 splits: a group's states are loaded at once (one round
+// of memory latency per group), then weighted by 2^(m_s - M) against the
+// exact maximum M so far, the running sums rescaled when M grows.  D / 4
+// lanes per row, four features per lane, 16-byte loads.
 constexpr int kCombineThreads = 256;
+constexpr int kCombineGroup = 16;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kCombineThreads) void splitkv_combine_kernel(
@@ -900,19 +902,35 @@ __global__ __launch_bounds__(kCombineThreads) void splitkv_combine_kernel(
   const int row = blockIdx.x * RPB + threadIdx.x / LPR;
   if (row >= rows) return;
   const f32x2* ml = reinterpret_cast<const f32x2*>(part_ml) + (int64_t)row * S;
-  float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s][0]);
+  const f32x4* pa = reinterpret_cast<const f32x4*>(part + (int64_t)row * S * D) + lr;
+  float M = kNegInf, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  if (M != kNegInf) {
-    const f32x4* pa = reinterpret_cast<const f32x4*>(part + (int64_t)row * S * D) + lr;
-  #pragma unroll 4
-    for (int s = 0; s < S; ++s) {
-      const f32x2 st = ml[s];
-      const float w = exp2_hw(st[0] - M);  // 0 for a split with no visible key
-      L += w * st[1];
-      acc += w * pa[s * LPR];
+  for (int s0 = 0; s0 < S; s0 += kCombineGroup) {
+    f32x2 st[kCombineGroup];
+    f32x4 x[kCombineGroup];
+    // Past the last split the loads repeat it (no branches between the
+    // loads) and its maximum is masked out, so its weight is 0.
+  #pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) {
+      const int sj = min(s0 + j, S - 1);
+      st[j] = ml[sj];
+      if (s0 + j >= S) st[j][0] = kNegInf;
+      x[j] = pa[sj * LPR];
     }
+    float mg = M;
+  #pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) mg = fmaxf(mg, st[j][0]);
+    if (mg == kNegInf) continue;  // no visible key in any split so far
+    const float r = exp2_hw(M - mg);  // 0 while M = -inf (L and acc are 0)
+    L *= r;
+    acc *= r;
+  #pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) {
+      const float w = exp2_hw(st[j][0] - mg);  // 0 for a split with no visible key
+      L += w * st[j][1];
+      acc += w * x[j];
+    }
+    M = mg;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   T o[4];

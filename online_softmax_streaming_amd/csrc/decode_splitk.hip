@@ -218,15 +218,14 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
 }
 
 // Folds the S split states of each row into out and (m, l), merge A1 over
-// groups of up to 16 splits: a group's states are loaded at once (one round
+// groups of G splits: a group's states are loaded at once (one round
 // of memory latency per group), then weighted by 2^(m_s - M) against the
 // exact maximum M so far, the running sums rescaled when M grows.  D / 2
 // lanes per row, two features per lane (8-byte loads: a split's a[D] starts
 // 8 bytes into its D + 2 floats).
 constexpr int kCombineThreads = 256;
-constexpr int kCombineGroup = 16;
 
-template <typename T, int D>
+template <typename T, int D, int G>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeArgs a, int rows) {
   constexpr int LPR = D / 2;
   constexpr int RPB = kCombineThreads / LPR;
@@ -236,13 +235,13 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
   const float* src = a.part + (int64_t)row * a.S * (D + 2);
   float M = kNegInf, L = 0.f;
   f32x2 acc = {0.f, 0.f};
-  for (int s0 = 0; s0 < a.S; s0 += kCombineGroup) {
-    float m[kCombineGroup], l[kCombineGroup];
-    f32x2 x[kCombineGroup];
+  for (int s0 = 0; s0 < a.S; s0 += G) {
+    float m[G], l[G];
+    f32x2 x[G];
     // Past the last split the loads repeat it (no branches between the
     // loads) and its maximum is masked out; its weight below is 0.
   #pragma unroll
-    for (int j = 0; j < kCombineGroup; ++j) {
+    for (int j = 0; j < G; ++j) {
       const float* st = src + min(s0 + j, a.S - 1) * (D + 2);
       m[j] = s0 + j < a.S ? st[0] : kNegInf;
       l[j] = st[1];
@@ -250,13 +249,13 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
     }
     float mg = M;
   #pragma unroll
-    for (int j = 0; j < kCombineGroup; ++j) mg = fmaxf(mg, m[j]);
+    for (int j = 0; j < G; ++j) mg = fmaxf(mg, m[j]);
     if (mg == kNegInf) continue;  // no visible key in any split so far
     const float r = exp2_hw(M - mg);  // 0 while M = -inf (L and acc are 0)
     L *= r;
     acc *= r;
   #pragma unroll
-    for (int j = 0; j < kCombineGroup; ++j) {
+    for (int j = 0; j < G; ++j) {
       const float w = exp2_hw(m[j] - mg);  // 0 for a split with no visible key
       L += w * l[j];
       acc += w * x[j];
@@ -309,8 +308,18 @@ hipError_t launch_typed(const Problem& p, const DecodePlan& plan, float* scratch
   }
   if (e != hipSuccess) return e;
   constexpr int RPB = kCombineThreads / (D / 2);
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)),
-                     dim3(kCombineThreads), 0, p.stream, a, (int)rows);
+  const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
+  // Groups no larger than the splits (a group past the last split repeats
+  // its loads): 4, 8 or 16.
+  if (plan.splits <= 4)
+    hipLaunchKernelGGL((decode_combine_kernel<T, D, 4>), grid, dim3(kCombineThreads), 0, p.stream,
+                       a, (int)rows);
+  else if (plan.splits <= 8)
+    hipLaunchKernelGGL((decode_combine_kernel<T, D, 8>), grid, dim3(kCombineThreads), 0, p.stream,
+                       a, (int)rows);
+  else
+    hipLaunchKernelGGL((decode_combine_kernel<T, D, 16>), grid, dim3(kCombineThreads), 0, p.stream,
+                       a, (int)rows);
   return hipGetLastError();
 }
 

@@ -885,14 +885,13 @@ hipError_t launch_t(const Problem& p) {
 }
 
 // Folds the S split states of each row into out and (m, l), merge A1 over
-// groups of up to 16 splits: a group's states are loaded at once (one round
+// groups of G splits: a group's states are loaded at once (one round
 // of memory latency per group), then weighted by 2^(m_s - M) against the
 // exact maximum M so far, the running sums rescaled when M grows.  D / 4
 // lanes per row, four features per lane, 16-byte loads.
 constexpr int kCombineThreads = 256;
-constexpr int kCombineGroup = 16;
 
-template <typename T, int D>
+template <typename T, int D, int G>
 __global__ __launch_bounds__(kCombineThreads) void splitkv_combine_kernel(
     const float* __restrict__ part, const float* __restrict__ part_ml, T* __restrict__ out,
     float* __restrict__ m_out, float* __restrict__ l_out, int rows, int S) {
@@ -905,13 +904,13 @@ __global__ __launch_bounds__(kCombineThreads) void splitkv_combine_kernel(
   const f32x4* pa = reinterpret_cast<const f32x4*>(part + (int64_t)row * S * D) + lr;
   float M = kNegInf, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += kCombineGroup) {
-    f32x2 st[kCombineGroup];
-    f32x4 x[kCombineGroup];
+  for (int s0 = 0; s0 < S; s0 += G) {
+    f32x2 st[G];
+    f32x4 x[G];
     // Past the last split the loads repeat it (no branches between the
     // loads) and its maximum is masked out, so its weight is 0.
   #pragma unroll
-    for (int j = 0; j < kCombineGroup; ++j) {
+    for (int j = 0; j < G; ++j) {
       const int sj = min(s0 + j, S - 1);
       st[j] = ml[sj];
       if (s0 + j >= S) st[j][0] = kNegInf;
@@ -919,13 +918,13 @@ __global__ __launch_bounds__(kCombineThreads) void splitkv_combine_kernel(
     }
     float mg = M;
   #pragma unroll
-    for (int j = 0; j < kCombineGroup; ++j) mg = fmaxf(mg, st[j][0]);
+    for (int j = 0; j < G; ++j) mg = fmaxf(mg, st[j][0]);
     if (mg == kNegInf) continue;  // no visible key in any split so far
     const float r = exp2_hw(M - mg);  // 0 while M = -inf (L and acc are 0)
     L *= r;
     acc *= r;
   #pragma unroll
-    for (int j = 0; j < kCombineGroup; ++j) {
+    for (int j = 0; j < G; ++j) {
       const float w = exp2_hw(st[j][0] - mg);  // 0 for a split with no visible key
       L += w * st[j][1];
       acc += w * x[j];
@@ -952,9 +951,20 @@ hipError_t launch_splitkv_d(const Problem& p) {
   if (e != hipSuccess) return e;
   const int64_t rows = p.B * p.H * p.Nq;
   constexpr int RPB = kCombineThreads / (D / 4);
-  hipLaunchKernelGGL((splitkv_combine_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)),
-                     dim3(kCombineThreads), 0, p.stream, p.part, p.part + rows * p.splits * D,
-                     static_cast<T*>(p.o), p.m_out, p.l_out, (int)rows, (int)p.splits);
+  const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
+  const float* ml = p.part + rows * p.splits * D;
+  T* o = static_cast<T*>(p.o);
+  // Groups no larger than the splits (a group past the last split repeats
+  // its loads): 4, 8 or 16.
+  if (p.splits <= 4)
+    hipLaunchKernelGGL((splitkv_combine_kernel<T, D, 4>), grid, dim3(kCombineThreads), 0,
+                       p.stream, p.part, ml, o, p.m_out, p.l_out, (int)rows, (int)p.splits);
+  else if (p.splits <= 8)
+    hipLaunchKernelGGL((splitkv_combine_kernel<T, D, 8>), grid, dim3(kCombineThreads), 0,
+                       p.stream, p.part, ml, o, p.m_out, p.l_out, (int)rows, (int)p.splits);
+  else
+    hipLaunchKernelGGL((splitkv_combine_kernel<T, D, 16>), grid, dim3(kCombineThreads), 0,
+                       p.stream, p.part, ml, o, p.m_out, p.l_out, (int)rows, (int)p.splits);
   return hipGetLastError();
 }
 

@@ -239,8 +239,8 @@ ATTN_API int attn_fwd_masked(const void* Q, const void* K, const void* V, void* 
  * p: 0 <= p < 1 and round(p * 65536) <= 65535 (else ATTN_E_INVALID); p = 0
  * gives attn_fwd_gqa's output bit for bit when that call also takes the
  * tiled kernels (a bf16/f16 problem too small to fill the GPU splits each
- * row's keys over several waves there, which rounds differently, within
- * the same tolerances).  Other arguments, layout,
+ * row's keys over several waves or workgroups there, which rounds
+ * differently, within the same tolerances).  Other arguments, layout,
  * errors as attn_fwd_gqa; m_out, l_out may be NULL.  Every Nq takes the
  * tiled kernels; the call allocates nothing.
  */

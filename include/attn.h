@@ -102,11 +102,10 @@ extern "C" {
  * such buffer per (device, stream), taken with hipMallocAsync on `stream`,
  * grown on demand in 1 MiB steps and held until the process ends; calls on
  * one stream reuse it in stream order, and every call that takes scratch
- * (this one, attn_bwd, attn_decode_paged, softmax_rows) shares it.  A
- * stream on which such a call may still run must be synchronised before it
- * is destroyed (a new stream may receive its handle, and with it the
- * buffer).
- * Under HIP graph capture each call instead takes its own hipMallocAsync /
+ * (this one, attn_fwd_varlen, attn_bwd, attn_decode_paged, softmax_rows)
+ * shares it.  A stream on which such a call may still run must be
+ * synchronised before it is destroyed (a new stream may receive its
+ * handle, and with it the buffer).  Under HIP graph capture each call instead takes its own hipMallocAsync /
  * hipFreeAsync pair, which become the graph's allocation nodes.  Callers
  * that cannot allocate at all use attn_decode_paged_noalloc.
  */
@@ -271,7 +270,9 @@ ATTN_API int attn_fwd_dropout(const void* Q, const void* K, const void* V, void*
  *
  * Arguments:
  *   max_seqlen_q  the longest query sequence (sizes the grid; 0 <= it <=
- *                 total_q).  Rows of a longer sequence are not written.
+ *                 total_q).  A longer sequence is outside the contract:
+ *                 some of its rows may be left unwritten (none is written
+ *                 wrong).
  *   cu_seqlens_*  device arrays, 4-byte aligned.  Values are not scanned:
  *                 each bound is clamped into [0, total] and made
  *                 non-decreasing, so no value addresses memory outside the
@@ -281,8 +282,16 @@ ATTN_API int attn_fwd_dropout(const void* Q, const void* K, const void* V, void*
  *   Limits: total_q, total_k, B*H*max_seqlen_q < 2^31; packed K (and V)
  *   at most 4 GiB (else ATTN_E_UNSUPPORTED).  B, H or total_q == 0 is a
  *   no-op.  D, causal, scale, dtype, stream as attn_fwd.
- * Memory: allocates nothing.  Returns ATTN_OK once queued, else the status
- * codes of attn_fwd.
+ * Paths: bf16/f16 calls of at most 64 query tiles of 256 rows (B * H *
+ * ceil(max_seqlen_q / 256)) over at least 2048 keys in all (total_k) split
+ * each query tile's keys over workgroups when the rows alone would leave
+ * CUs idle (the split-KV prefill of attn_fwd; the lengths are not read on
+ * the host, so total_k stands in for the longest sequence's key count);
+ * everything else takes the tiled prefill kernels.
+ * Memory: the tiled kernels allocate nothing; the split-KV prefill uses the
+ * per-stream scratch described under attn_fwd ((D + 2) FP32 values per
+ * row of H * total_q and split).  Returns ATTN_OK once queued, else the
+ * status codes of attn_fwd.
  */
 ATTN_API int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* out,
                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,

@@ -149,6 +149,22 @@ class ScratchLease {
   bool owned_ = false;
 };
 
+// The split-KV prefill (plan from plan_prefill_splitkv): partial states in
+// the stream's scratch, then their combine.
+int run_splitkv(attn::Problem& p, const attn::SplitKvPlan& sk) {
+  ScratchLease scratch;
+  hipError_t e = scratch.acquire(p.stream, sk.scratch_bytes);
+  if (e != hipSuccess) return hip_fail(e, "split-key scratch allocation");
+  p.part = scratch.ptr();
+  p.splits = sk.splits;
+  p.split_tiles = sk.split_tiles;
+  e = attn::launch_prefill_splitkv(p);
+  const hipError_t ef = scratch.release();
+  if (e != hipSuccess) return hip_fail(e, "split-key prefill launch");
+  if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of split-key scratch");
+  return ATTN_OK;
+}
+
 int run_attention(const void* Q, const void* K, const void* V, void* out, int64_t B, int64_t H,
                   int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
                   int dtype, float* m_out, float* l_out, void* stream,
@@ -254,19 +270,7 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
     return ATTN_OK;
   }
   attn::SplitKvPlan sk;
-  if (plain && dtype != ATTN_F32 && attn::plan_prefill_splitkv(p, &sk)) {
-    ScratchLease scratch;
-    e = scratch.acquire(p.stream, sk.scratch_bytes);
-    if (e != hipSuccess) return hip_fail(e, "split-key scratch allocation");
-    p.part = scratch.ptr();
-    p.splits = sk.splits;
-    p.split_tiles = sk.split_tiles;
-    e = attn::launch_prefill_splitkv(p);
-    const hipError_t ef = scratch.release();
-    if (e != hipSuccess) return hip_fail(e, "split-key prefill launch");
-    if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync of split-key scratch");
-    return ATTN_OK;
-  }
+  if (plain && dtype != ATTN_F32 && attn::plan_prefill_splitkv(p, &sk)) return run_splitkv(p, sk);
   e = dtype == ATTN_F32 ? attn::launch_prefill_f32(p) : attn::launch_prefill_mfma(p);
   return e == hipSuccess ? ATTN_OK : hip_fail(e, "prefill kernel launch");
 }
@@ -657,6 +661,9 @@ int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* out,
   p.cu_k = cu_seqlens_k;
   p.total_q = total_q;
   p.total_k = total_k;
+  attn::SplitKvPlan sk;
+  if (dtype != ATTN_F32 && total_k > 0 && attn::plan_prefill_splitkv(p, &sk))
+    return run_splitkv(p, sk);
   const hipError_t e =
       dtype == ATTN_F32 ? attn::launch_prefill_f32(p) : attn::launch_prefill_mfma(p);
   return e == hipSuccess ? ATTN_OK : hip_fail(e, "varlen prefill kernel launch");

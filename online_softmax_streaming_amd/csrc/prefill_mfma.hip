@@ -89,10 +89,11 @@ struct PrefillArgs {
   uint64_t seed, offset;
   uint32_t drop_t;
   float keep_gain;
-  // Split-key mode (SPLITKV kernels only, batched layout): work item (head,
-  // query tile, split s) covers key tiles [s * kpt, (s + 1) * kpt) and writes
-  // each row's state, FP32, base 2, l and a relative to the exact maximum m:
-  // a[D] to part[row][s][.], (m, l) to part_ml[row][s][.].
+  // Split-key mode (SPLITKV kernels only, batched or packed layout): work
+  // item (head, query tile, split s) covers key tiles [s * kpt, (s + 1) *
+  // kpt) and writes each row's state, FP32, base 2, l and a relative to the
+  // exact maximum m: a[D] to part[row][s][.], (m, l) to part_ml[row][s][.],
+  // rows in row-state order.
   float* part;
   float* part_ml;
   int S;    // splits per row
@@ -101,9 +102,16 @@ struct PrefillArgs {
 
 // Kernel modes: batched [B, H, N, D]; packed variable-length sequences;
 // batched with an arbitrary mask and/or a sliding window; batched with
-// dropout on the probabilities; batched with the keys split over
+// dropout on the probabilities; batched or packed with the keys split over
 // workgroups (partial states to scratch).
-enum : int { kModeBatched = 0, kModeVarlen = 1, kModeMasked = 2, kModeDropout = 3, kModeSplitKv = 4 };
+enum : int {
+  kModeBatched = 0,
+  kModeVarlen = 1,
+  kModeMasked = 2,
+  kModeDropout = 3,
+  kModeSplitKv = 4,
+  kModeVarlenSplitKv = 5
+};
 
 constexpr int kBN = 64;              // keys per tile
 // LDS operand reads in flight ahead of the MFMA that uses them.
@@ -125,10 +133,10 @@ template <int NW> constexpr int kWavesPerEu = NW >= 16 ? 4 : 2;
 template <typename T, int D, int NW, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<NW>)))
 void prefill_mfma_kernel(PrefillArgs a) {
-  constexpr bool VARLEN = MODE == kModeVarlen;
+  constexpr bool VARLEN = MODE == kModeVarlen || MODE == kModeVarlenSplitKv;
   constexpr bool MASKED = MODE == kModeMasked;
   constexpr bool DROPOUT = MODE == kModeDropout;
-  constexpr bool SPLITKV = MODE == kModeSplitKv;
+  constexpr bool SPLITKV = MODE == kModeSplitKv || MODE == kModeVarlenSplitKv;
   typedef typename Mfma<T>::vec8 vec8;
   typedef typename Mfma<T>::vec4 vec4;
   typedef typename Mfma<T>::vec2 vec2;
@@ -222,7 +230,8 @@ void prefill_mfma_kernel(PrefillArgs a) {
     Nq = q1 - q0;
     Nk = k1 - k0;
     nqt = (Nq + BM - 1) / BM;
-    if (rr >= (CAUSAL ? (nqt + 1) / 2 : nqt)) return;  // shorter than the longest sequence
+    // Shorter than the longest sequence.
+    if (rr >= (SPLITKV ? nqt * a.S : CAUSAL ? (nqt + 1) / 2 : nqt)) return;
     sq = (int64_t)a.H * D;
     sk = (int64_t)a.Hkv * D;
     qbase = (int64_t)q0 * sq + (int64_t)h * D;
@@ -784,10 +793,13 @@ hipError_t launch_typed(const Problem& p) {
   a.drop_t = p.drop_t;
   a.keep_gain = (float)(65536.0 / (65536.0 - (double)p.drop_t));
   a.part = p.part;
-  a.part_ml = p.part ? p.part + p.B * p.H * p.Nq * p.splits * D : nullptr;
+  const int64_t state_rows = p.cu_q ? p.H * p.total_q : p.B * p.H * p.Nq;
+  a.part_ml = p.part ? p.part + state_rows * p.splits * D : nullptr;
   a.S = (int)p.splits;
   a.kpt = (int)p.split_tiles;
-  a.nwork = MODE == kModeSplitKv ? a.nqt * a.S : CAUSAL ? (a.nqt + 1) / 2 : a.nqt;
+  a.nwork = MODE == kModeSplitKv || MODE == kModeVarlenSplitKv ? a.nqt * a.S
+            : CAUSAL                                         ? (a.nqt + 1) / 2
+                                                             : a.nqt;
   const int64_t total = p.B * p.H * a.nwork;
   a.total = (int)total;
   const int64_t grid = (total + 7) / 8 * 8;
@@ -894,12 +906,35 @@ constexpr int kCombineThreads = 256;
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kCombineThreads) void splitkv_combine_kernel(
     const float* __restrict__ part, const float* __restrict__ part_ml, T* __restrict__ out,
-    float* __restrict__ m_out, float* __restrict__ l_out, int rows, int S) {
+    float* __restrict__ m_out, float* __restrict__ l_out, int rows, int S, const int* cu_q, int H,
+    int total_q, int row_span, int causal) {
   constexpr int LPR = D / 4;
   constexpr int RPB = kCombineThreads / LPR;
   const int lr = threadIdx.x % LPR;
-  const int row = blockIdx.x * RPB + threadIdx.x / LPR;
-  if (row >= rows) return;
+  int row;       // row-state index
+  int64_t orow;  // output row
+  if (cu_q) {
+    // Packed sequences: workgroup (sequence b, head h, chunk c) takes rows
+    // c * RPB .. of the sequence, as far as the split kernel wrote states:
+    // its row_span / BM query tiles of BM rows, which under causal masking
+    // end at the sequence's last row, so the first tile starts pad rows
+    // before row 0 (sequence bounds clamped as there).
+    const int nchunk = row_span / RPB;
+    const int bh = blockIdx.x / nchunk;
+    const int b = bh / H, h = bh - b * H;
+    const int i = (blockIdx.x - bh * nchunk) * RPB + threadIdx.x / LPR;
+    const int q0 = min(max(cu_q[b], 0), total_q);
+    const int q1 = min(max(cu_q[b + 1], q0), total_q);
+    constexpr int BM = 32 * kWaves;
+    const int pad = causal ? (BM - (q1 - q0) % BM) % BM : 0;
+    if (i >= q1 - q0 || i >= row_span - pad) return;
+    row = h * total_q + q0 + i;
+    orow = (int64_t)(q0 + i) * H + h;
+  } else {
+    row = blockIdx.x * RPB + threadIdx.x / LPR;
+    if (row >= rows) return;
+    orow = row;
+  }
   const f32x2* ml = reinterpret_cast<const f32x2*>(part_ml) + (int64_t)row * S;
   const f32x4* pa = reinterpret_cast<const f32x4*>(part + (int64_t)row * S * D) + lr;
   float M = kNegInf, L = 0.f;
@@ -937,7 +972,7 @@ __global__ __launch_bounds__(kCombineThreads) void splitkv_combine_kernel(
   for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(acc[j] * inv);
   u32x2 bits;
   __builtin_memcpy(&bits, o, sizeof(bits));
-  *reinterpret_cast<u32x2*>(out + (int64_t)row * D + 4 * lr) = bits;
+  *reinterpret_cast<u32x2*>(out + orow * D + 4 * lr) = bits;
   if (lr == 0) {
     if (m_out) m_out[row] = M * kLn2;
     if (l_out) l_out[row] = L;
@@ -946,25 +981,35 @@ __global__ __launch_bounds__(kCombineThreads) void splitkv_combine_kernel(
 
 template <typename T, int D>
 hipError_t launch_splitkv_d(const Problem& p) {
-  const hipError_t e = p.causal ? launch_typed<T, D, kWaves, true, kModeSplitKv>(p)
-                                : launch_typed<T, D, kWaves, false, kModeSplitKv>(p);
+  hipError_t e;
+  if (p.cu_q)
+    e = p.causal ? launch_typed<T, D, kWaves, true, kModeVarlenSplitKv>(p)
+                 : launch_typed<T, D, kWaves, false, kModeVarlenSplitKv>(p);
+  else
+    e = p.causal ? launch_typed<T, D, kWaves, true, kModeSplitKv>(p)
+                 : launch_typed<T, D, kWaves, false, kModeSplitKv>(p);
   if (e != hipSuccess) return e;
-  const int64_t rows = p.B * p.H * p.Nq;
+  const int64_t rows = p.cu_q ? p.H * p.total_q : p.B * p.H * p.Nq;
+  // Packed: rows of each (sequence, head) up to the split kernel's tiles.
+  const int span = (int)((p.Nq + 32 * kWaves - 1) / (32 * kWaves) * (32 * kWaves));
   constexpr int RPB = kCombineThreads / (D / 4);
-  const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
+  const dim3 grid((unsigned)(p.cu_q ? p.B * p.H * (span / RPB) : (rows + RPB - 1) / RPB));
   const float* ml = p.part + rows * p.splits * D;
   T* o = static_cast<T*>(p.o);
   // Groups no larger than the splits (a group past the last split repeats
   // its loads): 4, 8 or 16.
+  auto launch = [&](auto group) {
+    constexpr int G = decltype(group)::value;
+    hipLaunchKernelGGL((splitkv_combine_kernel<T, D, G>), grid, dim3(kCombineThreads), 0, p.stream,
+                       p.part, ml, o, p.m_out, p.l_out, (int)rows, (int)p.splits, p.cu_q,
+                       (int)p.H, (int)p.total_q, span, p.causal ? 1 : 0);
+  };
   if (p.splits <= 4)
-    hipLaunchKernelGGL((splitkv_combine_kernel<T, D, 4>), grid, dim3(kCombineThreads), 0,
-                       p.stream, p.part, ml, o, p.m_out, p.l_out, (int)rows, (int)p.splits);
+    launch(std::integral_constant<int, 4>{});
   else if (p.splits <= 8)
-    hipLaunchKernelGGL((splitkv_combine_kernel<T, D, 8>), grid, dim3(kCombineThreads), 0,
-                       p.stream, p.part, ml, o, p.m_out, p.l_out, (int)rows, (int)p.splits);
+    launch(std::integral_constant<int, 8>{});
   else
-    hipLaunchKernelGGL((splitkv_combine_kernel<T, D, 16>), grid, dim3(kCombineThreads), 0,
-                       p.stream, p.part, ml, o, p.m_out, p.l_out, (int)rows, (int)p.splits);
+    launch(std::integral_constant<int, 16>{});
   return hipGetLastError();
 }
 
@@ -986,9 +1031,15 @@ bool plan_prefill_splitkv(const Problem& p, SplitKvPlan* plan) {
   // tiles: few query tiles over many keys cannot fill the GPU by rows, so
   // their keys are split over workgroups, each split at least
   // SPLITKV_MIN_TILES key tiles long, for about one workgroup per CU.
+  // Packed sequences: the host does not read the sequence lengths, so the
+  // plan takes every sequence as long as the longest query sequence over
+  // total_k keys (exact for one sequence); splits past a shorter sequence's
+  // keys write empty states.
+  const bool packed = p.cu_q != nullptr;
+  const int64_t nk = packed ? p.total_k : p.Nk;
   const int64_t nqt = (p.Nq + 32 * kWaves - 1) / (32 * kWaves);
   const int64_t wq = p.B * p.H * nqt;
-  const int64_t kt = (p.Nk + kBN - 1) / kBN;
+  const int64_t kt = (nk + kBN - 1) / kBN;
   if (wq > SPLITKV_MAX_WQ || kt < 2 * SPLITKV_MIN_TILES) return false;
   int64_t S = (SPLITKV_TARGET_WGS + wq - 1) / wq;
   if (S > kt / SPLITKV_MIN_TILES) S = kt / SPLITKV_MIN_TILES;
@@ -997,9 +1048,10 @@ bool plan_prefill_splitkv(const Problem& p, SplitKvPlan* plan) {
   S = (kt + kpt - 1) / kpt;
   // Rows x keys streamed by the busiest CU, here (padding rows of the
   // 256-row tiles included) and on the route launch_prefill_mfma takes
-  // otherwise: the key-split kernel, one four-wave workgroup per 32-row
-  // block over all keys, or at D = 128 with 64 eight-wave workgroups,
-  // four-wave tiled workgroups of 128 rows (two tiles each when causal).
+  // otherwise: the key-split kernel (batched layout), one four-wave
+  // workgroup per 32-row block over all keys, or four-wave tiled workgroups
+  // of 128 rows (two tiles each when causal): packed sequences, and D = 128
+  // with 64 eight-wave workgroups.
   // Split keys when that load is lower; at D = 128 also when it is equal,
   // where the tiled kernel's two waves per SIMD beat the key-split
   // kernel's one (B1 H32 Nq512 Nk8192 causal 125 -> 88 us, B1 H8 Nq1024
@@ -1014,18 +1066,19 @@ bool plan_prefill_splitkv(const Problem& p, SplitKvPlan* plan) {
   const int64_t w8 = bh * (p.causal ? (nqt + 1) / 2 : nqt);
   const int64_t small = p.D > 64 ? kSmallGridWgs<128> : kSmallGridWgs<64>;
   int64_t other;
-  if (w8 <= small) {
-    other = per_cu(bh * ((p.Nq + 31) / 32)) * 32 * p.Nk;
+  if (!packed && w8 <= small) {
+    other = per_cu(bh * ((p.Nq + 31) / 32)) * 32 * nk;
   } else {
     const int64_t nqt4 = (p.Nq + 127) / 128;
     const bool pair = p.causal && nqt4 > 1;
-    other = per_cu(bh * (p.causal ? (nqt4 + 1) / 2 : nqt4)) * (pair ? 256 : 128) * p.Nk;
+    other = per_cu(bh * (p.causal ? (nqt4 + 1) / 2 : nqt4)) * (pair ? 256 : 128) * nk;
   }
   const int64_t mine = per_cu(wq * S) * 32 * kWaves * kpt * kBN;
   if (mine > other || (mine == other && p.D <= 64)) return false;
   plan->splits = S;
   plan->split_tiles = kpt;
-  plan->scratch_bytes = (size_t)(p.B * p.H * p.Nq) * (size_t)S * (size_t)(p.D + 2) * sizeof(float);
+  const int64_t rows = packed ? p.H * p.total_q : p.B * p.H * p.Nq;
+  plan->scratch_bytes = (size_t)rows * (size_t)S * (size_t)(p.D + 2) * sizeof(float);
   return true;
 }
 

@@ -110,3 +110,40 @@ def test_many_short_sequences(lib):
     lens = [int(x) for x in rng.integers(1, 300, size=40)]
     inputs = make_varlen(lens, lens, 4, 1, 64, "f16", seed=4, device="cuda")
     _check(lib, inputs, True, "f16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("h,hkv,d,lens_q,lens_k", [
+    (4, 2, 128, [512], [8192]),                 # one chunk over a long context: 8 splits
+    (4, 1, 64, [300, 100], [5000, 2000]),       # the shorter sequence's late splits are empty
+    (2, 2, 128, [200, 0, 50], [6000, 3000, 0]),  # no rows; no keys
+    (2, 1, 32, [64], [16384]),
+])
+def test_split_kv(lib, dtype, causal, h, hkv, d, lens_q, lens_k):
+    # Few query tiles over many keys: each tile's keys are split over
+    # workgroups (the plan takes total_k as the longest sequence's key
+    # count) and the partial states combined per sequence.
+    inputs = make_varlen(lens_q, lens_k, h, hkv, d, dtype, seed=sum(lens_k) + d, device="cuda")
+    _check(lib, inputs, causal, dtype)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_kv_longer_sequence_never_wrong(lib, causal):
+    # max_seqlen_q = 256 with a 300-row sequence: the rows of that sequence
+    # past the query tiles the grid holds are left as they were (noncausal:
+    # rows 256..; causal, tiles aligned to the last row: rows 44..), every
+    # other row matches the oracle, and no row is written wrong.
+    q, k, v, cu_q, cu_k = make_varlen([300, 40], [9000, 3000], 4, 4, 64, "bf16", seed=11,
+                                      device="cuda")
+    out = torch.full_like(q, 7.0)
+    lib.attn_fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q=256, causal=causal, out=out)
+    torch.cuda.synchronize()
+    scale = lib.default_scale(64)
+    want, _, _ = oracle.attention_varlen(_np(q), _np(k), _np(v), _np(cu_q), _np(cu_k), causal,
+                                         scale)
+    got = _np(out)
+    skipped = np.zeros(got.shape[0], dtype=bool)
+    skipped[(44 if causal else 256):300] = True
+    assert np.all(got[skipped] == 7.0)
+    assert float(np.max(np.abs(got[~skipped] - want[~skipped]))) <= TOL["bf16"]

@@ -1,14 +1,14 @@
-"""The prefill path under HIP graph capture.
+"""attn_fwd and attn_fwd_stats under HIP graph capture.
 
-The shapes here take the tiled prefill path of attn_fwd and attn_fwd_stats
-(more than 8 query rows, and not the bf16/f16 route of up to 32 rows per
-head over 8192 or more keys, which takes the split-key decode path and its
-stream-ordered scratch).  The prefill path allocates nothing and launches
-only kernels on the caller's stream, so the calls can be captured into a
-graph and replayed.  Each
-test captures calls once, replays the graph several times with eager work
-and synchronisations between the replays, and checks every replay bit for
-bit against an eager call on the same inputs (the kernel is deterministic),
+Most shapes here take the tiled prefill kernels, which allocate nothing and
+launch only kernels on the caller's stream.  Two take the paths with
+partial states: the split-KV prefill (few query tiles over many keys) and
+the split-key decode (few rows); under capture each such call takes its own
+hipMallocAsync / hipFreeAsync pair, which the graph records as allocation
+nodes (outside capture they use the stream's cached scratch).  Each test
+captures calls once, replays the graph several times with eager work and
+synchronisations between the replays, and checks every replay bit for bit
+against an eager call on the same inputs (the kernels are deterministic),
 including after the captured input buffers were refilled in place.  The
 eager result itself is checked against the FP64 oracle on one small case.
 """

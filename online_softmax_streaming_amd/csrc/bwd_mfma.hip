@@ -77,6 +77,12 @@ struct BwdArgs {
   int per_xcd;  // gridDim.x / 8
   float c;      // scale * log2(e)
   float scale;
+  // dQ with the keys split over workgroups (SPLIT dQ kernels): work item
+  // (head, query tile, split s) covers key tiles [s * kpt, (s + 1) * kpt)
+  // and writes its FP32 share of dQ to dq_part[s][row][.], rows = B*H*Nq.
+  float* dq_part;
+  int S, kpt;
+  int64_t rows;
 };
 
 constexpr int kBT = 64;  // rows of every streamed tile (keys in dq, queries in dkdv)
@@ -179,7 +185,7 @@ __device__ __forceinline__ void stage_pair(const T* x, const T* y, int rows, int
 // ---------------------------------------------------------------------------
 // Kernel 1: dQ, plus (lse2, Delta) per row.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NW, bool CAUSAL>
+template <typename T, int D, int NW, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(BwdArgs a) {
   typedef typename Mfma<T>::vec8 vec8;
@@ -205,10 +211,11 @@ void bwd_dq_kernel(BwdArgs a) {
   const int bh = logical / a.nwork;
   const int rr = logical - bh * a.nwork;
   // Causal: query tile ntile-1-r, then tile r, so workgroups stream equal
-  // numbers of key tiles.
-  const int npass = CAUSAL && a.ntile - 1 - rr != rr ? 2 : 1;
+  // numbers of key tiles.  Split: one query tile, split sp of its keys.
+  const int sp = SPLIT ? rr % a.S : 0;
+  const int npass = !SPLIT && CAUSAL && a.ntile - 1 - rr != rr ? 2 : 1;
   for (int pass = 0; pass < npass; ++pass) {
-    const int qt = CAUSAL ? (pass == 0 ? a.ntile - 1 - rr : rr) : rr;
+    const int qt = SPLIT ? rr / a.S : CAUSAL ? (pass == 0 ? a.ntile - 1 - rr : rr) : rr;
     const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
     const int64_t qbase = (int64_t)bh * Nq * D;
     const T* __restrict__ Qh = static_cast<const T*>(a.q) + qbase;
@@ -250,7 +257,7 @@ void bwd_dq_kernel(BwdArgs a) {
       const int64_t row = (int64_t)bh * Nq + qrow;
       const float ll = a.l[row];
       lse2 = ll > 0.f ? __builtin_fmaf(a.m[row], kLog2e, log2f(ll)) : kPosInf;
-      if (h32 == 0) {
+      if (h32 == 0 && sp == 0) {
         a.stat[2 * row] = lse2;
         a.stat[2 * row + 1] = dlt;
       }
@@ -258,7 +265,10 @@ void bwd_dq_kernel(BwdArgs a) {
 
     int kend = Nk;
     if (CAUSAL) kend = min(Nk, min(i0 + BM, Nq) + off);
-    const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+    const int nvis = kend > 0 ? (kend + BN - 1) / BN : 0;
+    // Key tiles [t_first, ntiles) of this work item.
+    const int t_first = SPLIT ? sp * a.kpt : 0;
+    const int ntiles = SPLIT ? min(nvis, t_first + a.kpt) : nvis;
 
     int koff[KC];
 #pragma unroll
@@ -346,8 +356,9 @@ void bwd_dq_kernel(BwdArgs a) {
     };
 
     const uint32_t kv_rows = (uint32_t)Nk;
-    if (ntiles > 0) {
-      stage_pair<T, D, NT>(Kh, Vh, (int)kv_rows, 0, tile_ptr(0, 0), tile_ptr(0, 1), tid, wave);
+    if (ntiles > t_first) {
+      stage_pair<T, D, NT>(Kh, Vh, (int)kv_rows, t_first * BN, tile_ptr(0, 0), tile_ptr(0, 1), tid,
+                           wave);
       __syncthreads();
       const int q_last = min(qw0 + 32, Nq) - 1;
       auto step = [&](auto bufc, int t) {
@@ -363,15 +374,28 @@ void bwd_dq_kernel(BwdArgs a) {
         }
         __syncthreads();
       };
-      for (int t = 0; t < ntiles; t += 2) {
+      for (int t = t_first; t < ntiles; t += 2) {
         step(std::integral_constant<int, 0>{}, t);
         if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
       }
     }
 
     // dQ = scale * (dS K): lane holds features n*32 + 8g + 4*h32 + 0..3 of
-    // its query row.
-    if (real) {
+    // its query row.  Split: this split's FP32 share.
+    if (SPLIT && real) {
+      float* row = a.dq_part + ((int64_t)sp * a.rows + (int64_t)bh * Nq + qrow) * D;
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = n * 32 + g * 8 + h32 * 4;
+          if (d0 < D)
+            *reinterpret_cast<f32x4*>(row + d0) =
+                f32x4{acc[n][g * 4] * a.scale, acc[n][g * 4 + 1] * a.scale,
+                      acc[n][g * 4 + 2] * a.scale, acc[n][g * 4 + 3] * a.scale};
+        }
+      }
+    } else if (real) {
       T* row = dQh + (int64_t)qrow * D;
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
@@ -704,6 +728,69 @@ void bwd_dkdv_kernel(BwdArgs a) {
 constexpr int kQWaves = ATTN_BWD_Q_WAVES;
 constexpr int kKVWaves = ATTN_BWD_KV_WAVES;
 
+// dQ of a split dQ pass: the sum of the S FP32 shares, one cast; four
+// features per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void dq_reduce_kernel(const float* __restrict__ part,
+                                                        T* __restrict__ dq, int64_t n4,
+                                                        int S) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4* src = reinterpret_cast<const f32x4*>(part) + i;
+  f32x4 acc = src[0];
+  for (int s = 1; s < S; ++s) acc += src[(int64_t)s * n4];
+  T o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(acc[j]);
+  u32x2 bits;
+  __builtin_memcpy(&bits, o, sizeof(bits));
+  reinterpret_cast<u32x2*>(dq)[i] = bits;
+}
+
+// Key splits of the dQ pass (1: no split).  Few 256-row query tiles over
+// many keys cannot fill the GPU by rows (dQ of a chunk of rows over a long
+// context), so their keys are split over about one eight-wave workgroup per
+// CU, at least 16 key tiles each, when that puts fewer rows x keys on the
+// busiest CU than the unsplit pass (four-wave workgroups of 128 rows, two
+// tiles each when causal, up to 128 eight-wave workgroups).
+struct DqSplit {
+  int S = 1, kpt = 0;
+};
+
+DqSplit plan_dq_split(const BwdProblem& p) {
+  DqSplit r;
+  if (p.dtype == DType::F32 || p.Nq <= 0 || p.Nk <= 0) return r;
+  const int64_t nqt = (p.Nq + 255) / 256;
+  const int64_t wq = p.B * p.H * nqt;
+  const int64_t kt = (p.Nk + kBT - 1) / kBT;
+  if (wq > 64 || kt < 32) return r;
+  int64_t S = (256 + wq - 1) / wq;
+  if (S > kt / 16) S = kt / 16;
+  if (S < 2) return r;
+  const int64_t kpt = (kt + S - 1) / S;
+  S = (kt + kpt - 1) / kpt;
+  auto per_cu = [](int64_t w) { return (w + 255) / 256; };
+  const int64_t bh = p.B * p.H;
+  const int64_t w8 = bh * (p.causal ? (nqt + 1) / 2 : nqt);
+  int64_t other;
+  if (w8 <= 128) {
+    const int64_t nqt4 = (p.Nq + 127) / 128;
+    const bool pair = p.causal && nqt4 > 1;
+    other = per_cu(bh * (p.causal ? (nqt4 + 1) / 2 : nqt4)) * (pair ? 256 : 128) * p.Nk;
+  } else {
+    other = per_cu(w8) * (p.causal && nqt > 1 ? 512 : 256) * p.Nk;
+  }
+  const int64_t mine = per_cu(wq * S) * 256 * kpt * kBT;
+  if (mine >= other) return r;
+  r.S = (int)S;
+  r.kpt = (int)kpt;
+  return r;
+}
+
+// Scratch: (lse2, Delta) per row, then (split dQ pass) the FP32 shares,
+// 16-byte aligned.
+int64_t stat_floats(const BwdProblem& p) { return (p.B * p.H * p.Nq * 2 + 3) / 4 * 4; }
+
 void fill_grid(BwdArgs& a, int64_t heads, int ntile, bool causal, int64_t* grid) {
   a.ntile = ntile;
   a.nwork = causal ? (ntile + 1) / 2 : ntile;
@@ -715,7 +802,7 @@ void fill_grid(BwdArgs& a, int64_t heads, int ntile, bool causal, int64_t* grid)
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_typed(const BwdProblem& p, float* stat) {
-  BwdArgs a;
+  BwdArgs a{};
   a.q = p.q;
   a.k = p.k;
   a.v = p.v;
@@ -733,7 +820,28 @@ hipError_t launch_typed(const BwdProblem& p, float* stat) {
   a.c = p.scale * kLog2e;
   a.scale = p.scale;
   int64_t grid = 0;
-  if (p.Nq > 0) {
+  const DqSplit split = plan_dq_split(p);
+  if (p.Nq > 0 && split.S > 1) {
+    // Eight-wave workgroups of 256 rows, (head, query tile, split).
+    a.dq_part = stat + stat_floats(p);
+    a.S = split.S;
+    a.kpt = split.kpt;
+    a.rows = p.B * p.H * p.Nq;
+    fill_grid(a, p.B * p.H, (int)((p.Nq + 255) / 256), false, &grid);
+    a.nwork = a.ntile * a.S;
+    a.total = (int)(p.B * p.H * a.nwork);
+    grid = ((int64_t)a.total + 7) / 8 * 8;
+    a.per_xcd = (int)(grid / 8);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, 8, CAUSAL, true>), dim3((unsigned)grid), dim3(8 * 64),
+                       0, p.stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n4 = a.rows * D / 4;
+    hipLaunchKernelGGL((dq_reduce_kernel<T>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
+                       p.stream, a.dq_part, static_cast<T*>(p.dq), n4, a.S);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (p.Nq > 0) {
     constexpr int BM = 32 * kQWaves;
     fill_grid(a, p.B * p.H, (int)((p.Nq + BM - 1) / BM), CAUSAL, &grid);
     if (a.total <= 128) {
@@ -742,10 +850,10 @@ hipError_t launch_typed(const BwdProblem& p, float* stat) {
       // -> 222 us per backward, B1 H4 N8192 causal 478 -> 397 us; with 256
       // or more eight-wave workgroups the two are level.
       fill_grid(a, p.B * p.H, (int)((p.Nq + 127) / 128), CAUSAL, &grid);
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, 4, CAUSAL>), dim3((unsigned)grid), dim3(4 * 64), 0,
-                         p.stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, 4, CAUSAL, false>), dim3((unsigned)grid),
+                         dim3(4 * 64), 0, p.stream, a);
     } else {
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, kQWaves, CAUSAL>), dim3((unsigned)grid),
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, kQWaves, CAUSAL, false>), dim3((unsigned)grid),
                          dim3(kQWaves * 64), 0, p.stream, a);
     }
     const hipError_t e = hipGetLastError();
@@ -779,7 +887,11 @@ hipError_t launch_t(const BwdProblem& p, float* stat) {
 
 }  // namespace
 
-size_t bwd_scratch_bytes(const BwdProblem& p) { return (size_t)(p.B * p.H * p.Nq) * 8; }
+size_t bwd_scratch_bytes(const BwdProblem& p) {
+  const DqSplit split = plan_dq_split(p);
+  if (split.S < 2) return (size_t)(p.B * p.H * p.Nq) * 8;
+  return (size_t)(stat_floats(p) + (int64_t)split.S * p.B * p.H * p.Nq * p.D) * sizeof(float);
+}
 
 hipError_t launch_bwd_mfma(const BwdProblem& p, float* scratch) {
   if (p.dtype == DType::BF16) return launch_t<__bf16>(p, scratch);

@@ -196,6 +196,22 @@ def test_grouped_kv(lib, dtype, causal, h, hkv, nq, nk, d):
     _check(lib, q, k, v, do, causal, got)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("b,h,hkv,nq,nk,d", [
+    (1, 4, 4, 256, 8192, 128),   # 8 key splits of the dQ pass
+    (1, 2, 2, 300, 5000, 64),    # 4 splits, ragged query tile and last key tile
+    (1, 4, 1, 256, 4096, 128),   # grouped K/V
+    (1, 2, 2, 64, 4096, 32),
+])
+def test_dq_key_split(lib, dtype, causal, b, h, hkv, nq, nk, d):
+    # Few query tiles over many keys: the dQ pass splits each tile's keys
+    # over workgroups and sums their FP32 shares (dK, dV unchanged).
+    q, k, v, do = _inputs(b, h, hkv, nq, nk, d, dtype, seed=nq + nk + d)
+    got = _run(lib, q, k, v, do, causal)
+    _check(lib, q, k, v, do, causal, got)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_large_logits_and_rising_keys(lib, dtype):
     # Scores spread over tens of units and a key ramp: P spans many orders

@@ -49,7 +49,8 @@ struct Problem {
   uint32_t drop_t = 0;
   // Keys split over workgroups (launch_prefill_splitkv): `splits` splits of
   // `split_tiles` 64-key tiles; FP32 partial states in `part`: a[D] as
-  // [B*H*Nq][splits][D], then (m, l) as [B*H*Nq][splits][2].
+  // [rows][splits][D], then (m, l) as [rows][splits][2], rows in row-state
+  // order (B*H*Nq batched, H*total_q packed).
   float* part = nullptr;
   int64_t splits = 0, split_tiles = 0;
 };

@@ -1057,10 +1057,11 @@ bool plan_prefill_splitkv(const Problem& p, SplitKvPlan* plan) {
   // kernel's one (B1 H32 Nq512 Nk8192 causal 125 -> 88 us, B1 H8 Nq1024
   // Nk8192 65 -> 57 us); at D <= 64 an equal load goes either way (B1 H4
   // Nq256 Nk8192 causal 34 -> 29 us, B1 H8 Nq1024 Nk8192 34 -> 44 us) and
-  // stays with the key-split kernel.  Lower loads: B1 H8 Nq512 Nk16384 D128 causal 117 -> 55 us,
-  // B1 H1 Nq512 Nk65536 D64 causal 227 -> 49 us, B1 H4 Nq512 Nk32768 D16
-  // 78 -> 34 us; higher ones lose (B4 H8 Nq256 Nk4096 D128 causal 37 ->
-  // 44 us).
+  // stays with the key-split kernel.  Lower loads: B1 H8 Nq512 Nk16384
+  // D128 causal 117 -> 55 us, B1 H1 Nq512 Nk65536 D64 causal 227 -> 49 us,
+  // B1 H4 Nq512 Nk32768 D16 78 -> 34 us; higher ones lose (B4 H8 Nq256
+  // Nk4096 D128 causal 37 -> 44 us).  (Times with the first version of the
+  // combine and a scratch allocation per call, both since made faster.)
   auto per_cu = [](int64_t wgs) { return (wgs + kNumCUs - 1) / kNumCUs; };
   const int64_t bh = p.B * p.H;
   const int64_t w8 = bh * (p.causal ? (nqt + 1) / 2 : nqt);

@@ -1052,16 +1052,15 @@ bool plan_prefill_splitkv(const Problem& p, SplitKvPlan* plan) {
   // workgroup per 32-row block over all keys, or four-wave tiled workgroups
   // of 128 rows (two tiles each when causal): packed sequences, and D = 128
   // with 64 eight-wave workgroups.
-  // Split keys when that load is lower; at D = 128 also when it is equal,
-  // where the tiled kernel's two waves per SIMD beat the key-split
-  // kernel's one (B1 H32 Nq512 Nk8192 causal 125 -> 88 us, B1 H8 Nq1024
-  // Nk8192 65 -> 57 us); at D <= 64 an equal load goes either way (B1 H4
-  // Nq256 Nk8192 causal 34 -> 29 us, B1 H8 Nq1024 Nk8192 34 -> 44 us) and
-  // stays with the key-split kernel.  Lower loads: B1 H8 Nq512 Nk16384
-  // D128 causal 117 -> 55 us, B1 H1 Nq512 Nk65536 D64 causal 227 -> 49 us,
-  // B1 H4 Nq512 Nk32768 D16 78 -> 34 us; higher ones lose (B4 H8 Nq256
-  // Nk4096 D128 causal 37 -> 44 us).  (Times with the first version of the
-  // combine and a scratch allocation per call, both since made faster.)
+  // Split keys when that load is lower or equal: the tiled kernel runs two
+  // waves per SIMD where the key-split kernel runs one, which pays for the
+  // partial states and their combine (equal loads: B1 H32 Nq512 Nk8192 D128
+  // causal 126 -> 73 us, B1 H32 Nq256 Nk16384 D64 causal 63 -> 49 us, B1 H4
+  // N4096 D64 causal 36.6 -> 30.6 us, B1 H8 Nq1024 Nk8192 D64 34.1 -> 33.6
+  // us; lower loads: B1 H8 Nq512 Nk16384 D128 causal 117 -> 52 us, B1 H1
+  // Nq512 Nk65536 D64 causal 227 -> 31 us).  Higher loads lose (B4 H8 Nq256
+  // Nk4096 D128 causal 37 -> 44 us, B2 H8 Nq512 Nk4096 D64 causal 20 -> 34
+  // us, the latter before the combine and the scratch were made faster).
   auto per_cu = [](int64_t wgs) { return (wgs + kNumCUs - 1) / kNumCUs; };
   const int64_t bh = p.B * p.H;
   const int64_t w8 = bh * (p.causal ? (nqt + 1) / 2 : nqt);
@@ -1075,7 +1074,7 @@ bool plan_prefill_splitkv(const Problem& p, SplitKvPlan* plan) {
     other = per_cu(bh * (p.causal ? (nqt4 + 1) / 2 : nqt4)) * (pair ? 256 : 128) * nk;
   }
   const int64_t mine = per_cu(wq * S) * 32 * kWaves * kpt * kBN;
-  if (mine > other || (mine == other && p.D <= 64)) return false;
+  if (mine > other) return false;
   plan->splits = S;
   plan->split_tiles = kpt;
   const int64_t rows = packed ? p.H * p.total_q : p.B * p.H * p.Nq;

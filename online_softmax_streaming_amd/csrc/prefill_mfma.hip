@@ -828,6 +828,9 @@ constexpr int64_t kSmallGridWgs = D > 64 ? 63 : 64;
 #ifndef SPLITKV_MAX_WQ
 #define SPLITKV_MAX_WQ 64
 #endif
+#ifndef SPLITKV_MIN_KEY_TILES
+#define SPLITKV_MIN_KEY_TILES 32
+#endif
 #ifndef SPLITKV_MIN_TILES
 #define SPLITKV_MIN_TILES 16
 #endif
@@ -1029,8 +1032,7 @@ hipError_t launch_splitkv_t(const Problem& p) {
 bool plan_prefill_splitkv(const Problem& p, SplitKvPlan* plan) {
   // Query tiles of the eight-wave kernel (no causal pairing here) and key
   // tiles: few query tiles over many keys cannot fill the GPU by rows, so
-  // their keys are split over workgroups, each split at least
-  // SPLITKV_MIN_TILES key tiles long, for about one workgroup per CU.
+  // their keys are split over workgroups, for about one workgroup per CU.
   // Packed sequences: the host does not read the sequence lengths, so the
   // plan takes every sequence as long as the longest query sequence over
   // total_k keys (exact for one sequence); splits past a shorter sequence's
@@ -1040,9 +1042,15 @@ bool plan_prefill_splitkv(const Problem& p, SplitKvPlan* plan) {
   const int64_t nqt = (p.Nq + 32 * kWaves - 1) / (32 * kWaves);
   const int64_t wq = p.B * p.H * nqt;
   const int64_t kt = (nk + kBN - 1) / kBN;
-  if (wq > SPLITKV_MAX_WQ || kt < 2 * SPLITKV_MIN_TILES) return false;
+  if (wq > SPLITKV_MAX_WQ || kt < SPLITKV_MIN_KEY_TILES) return false;
   int64_t S = (SPLITKV_TARGET_WGS + wq - 1) / wq;
-  if (S > kt / SPLITKV_MIN_TILES) S = kt / SPLITKV_MIN_TILES;
+  // Splits of at least 16 key tiles; half that when the 16-tile splits
+  // would fill fewer than half the CUs (B1 H4 Nq256 Nk8192 D64 causal 24.3
+  // -> 19.0 us, B2 H1 Nq300 Nk12000 D128 37.1 -> 28.0 us; with shorter
+  // splits on every shape, B2 H4 N2048 D16 went 10.3 -> 14.2 us).
+  int64_t cap = kt / SPLITKV_MIN_TILES;
+  if (wq * (S < cap ? S : cap) < kNumCUs / 2) cap = kt / (SPLITKV_MIN_TILES / 2);
+  if (S > cap) S = cap;
   if (S < 2) return false;
   const int64_t kpt = (kt + S - 1) / S;
   S = (kt + kpt - 1) / kpt;

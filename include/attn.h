@@ -91,11 +91,11 @@ extern "C" {
  *
  * Paths: Nq <= 8 takes the split-key decode path (keys split across
  * workgroups, partial states merged); so does bf16/f16 with Nq <= 32,
- * (H / Hkv) * Nq <= 64 and Nk >= 8192.  bf16/f16 problems of at most 64
- * query tiles of 256 rows over at least 2048 keys, whose rows alone would
- * leave CUs idle, split each query tile's keys over workgroups the same
- * way (split-KV prefill).  Everything else takes the tiled prefill
- * kernels.
+ * (H / Hkv) * Nq <= 64 and Nk >= 8192.  Problems whose rows alone would
+ * leave CUs idle (bf16/f16: at most 64 query tiles of 256 rows over at
+ * least 2048 keys; FP32: fewer than 512 default workgroups over at least
+ * 1024 keys) split each query tile's keys over workgroups the same way
+ * (split-KV prefill).  Everything else takes the tiled prefill kernels.
  * Memory: the tiled prefill kernels allocate nothing.  The split-key decode
  * path and the split-KV prefill need a scratch array of partial states
  * (FP32, (D + 2) floats per query row and split).  The library keeps one

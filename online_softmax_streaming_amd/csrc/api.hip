@@ -270,7 +270,7 @@ int run_attention(const void* Q, const void* K, const void* V, void* out, int64_
     return ATTN_OK;
   }
   attn::SplitKvPlan sk;
-  if (plain && dtype != ATTN_F32 && attn::plan_prefill_splitkv(p, &sk)) return run_splitkv(p, sk);
+  if (plain && attn::plan_prefill_splitkv(p, &sk)) return run_splitkv(p, sk);
   e = dtype == ATTN_F32 ? attn::launch_prefill_f32(p) : attn::launch_prefill_mfma(p);
   return e == hipSuccess ? ATTN_OK : hip_fail(e, "prefill kernel launch");
 }

@@ -57,10 +57,10 @@ struct Problem {
 
 // Streaming prefill on bf16/f16 matrix cores (prefill_mfma.hip).
 hipError_t launch_prefill_mfma(const Problem& p);
-// Plain bf16/f16 prefill with the keys of each query tile split over
-// workgroups, for few long rows (prefill_mfma.hip): whether to take it, and
-// its splits; then the tiled kernel writes partial states to p.part and a
-// combine kernel folds them, on p.stream.
+// Plain prefill with the keys of each query tile split over workgroups, for
+// few long rows (prefill_mfma.hip): whether to take it, and its splits; then
+// the tiled kernel (bf16/f16) or the FP32 kernel writes partial states to
+// p.part and a combine kernel folds them, on p.stream.
 struct SplitKvPlan {
   int64_t splits;
   int64_t split_tiles;
@@ -68,6 +68,10 @@ struct SplitKvPlan {
 };
 bool plan_prefill_splitkv(const Problem& p, SplitKvPlan* plan);
 hipError_t launch_prefill_splitkv(const Problem& p);
+// The FP32 form (prefill_f32.hip): plan, and the vector-ALU kernel's
+// partial states (launch_prefill_splitkv then combines them).
+bool plan_prefill_f32_splitkv(const Problem& p, SplitKvPlan* plan);
+hipError_t launch_prefill_f32_partials(const Problem& p);
 // Streaming prefill for FP32 inputs on the vector ALUs (prefill_f32.hip).
 hipError_t launch_prefill_f32(const Problem& p);
 

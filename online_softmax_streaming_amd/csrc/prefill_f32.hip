@@ -48,9 +48,16 @@ struct F32Args {
   uint64_t seed, offset;
   uint32_t drop_t;
   float keep_gain;
+  // Split-key mode (batched layout): workgroup (head, query tile, split s)
+  // covers key tiles [s * kpt, (s + 1) * kpt) and writes each row's state,
+  // base 2, l and a relative to the exact maximum m: a[D] to
+  // part[row][s][.], (m, l) to part_ml[row][s][.].
+  float* part;
+  float* part_ml;
+  int S, kpt;
 };
 
-enum : int { kModeBatched = 0, kModeVarlen = 1, kModeMasked = 2, kModeDropout = 3 };
+enum : int { kModeBatched = 0, kModeVarlen = 1, kModeMasked = 2, kModeDropout = 3, kModeSplitKv = 4 };
 
 constexpr int kThreads = 128;
 constexpr int kBNF = 32;
@@ -88,14 +95,18 @@ __global__ __launch_bounds__(NT * KSF) void prefill_f32_kernel(F32Args a) {
   constexpr bool VARLEN = MODE == kModeVarlen;
   constexpr bool MASKED = MODE == kModeMasked;
   constexpr bool DROPOUT = MODE == kModeDropout;
+  constexpr bool SPLITKV = MODE == kModeSplitKv;
   constexpr int DT = D / TPQ;
   constexpr int QPB = NT / TPQ;
 
   __shared__ __attribute__((aligned(16))) float Ksm[KSF][BN * D];
   __shared__ __attribute__((aligned(16))) float Vsm[KSF][BN * D];
 
-  const int bh = blockIdx.x / a.nqt;
-  const int qt = blockIdx.x - bh * a.nqt;
+  const int nwork = SPLITKV ? a.nqt * a.S : a.nqt;
+  const int bh = blockIdx.x / nwork;
+  const int rr = blockIdx.x - bh * nwork;
+  const int qt = SPLITKV ? rr / a.S : rr;
+  const int sp = SPLITKV ? rr - qt * a.S : 0;
   int Nq = a.Nq, Nk = a.Nk;
   int64_t qbase, kbase, stat0, sq = D, sk = D;
   if (VARLEN) {
@@ -143,9 +154,10 @@ __global__ __launch_bounds__(NT * KSF) void prefill_f32_kernel(F32Args a) {
 
   int kend = Nk;
   if (CAUSAL) kend = min(Nk, min(i0 + QPB, Nq) + off);
-  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  const int nvis = kend > 0 ? (kend + BN - 1) / BN : 0;
   const int win = MASKED ? a.window : 0;
-  const int t_first = win > 0 ? max(0, i0 + off - win + 1) / BN : 0;
+  const int t_first = SPLITKV ? sp * a.kpt : win > 0 ? max(0, i0 + off - win + 1) / BN : 0;
+  const int ntiles = SPLITKV ? min(nvis, t_first + a.kpt) : nvis;
   const uint32_t* mrow = nullptr;
   if (MASKED && a.mask && qrow < Nq) {
     const int b = bh / a.H, h = bh - b * a.H;
@@ -263,6 +275,20 @@ __global__ __launch_bounds__(NT * KSF) void prefill_f32_kernel(F32Args a) {
     m_run = M;
   }
 
+  if (SPLITKV) {
+    // The split's state (a = 0, l = 0, m = -inf for a row that sees no key
+    // of the split).
+    if (qrow < Nq) {
+      const int64_t st = (stat0 + qrow) * a.S + sp;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) a.part[st * D + part * DT + d] = acc[d];
+      if (part == 0) {
+        a.part_ml[2 * st] = m_run;
+        a.part_ml[2 * st + 1] = l_run;
+      }
+    }
+    return;
+  }
   if (qrow < Nq) {
     float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     if (DROPOUT) inv *= a.keep_gain;
@@ -306,7 +332,11 @@ hipError_t launch_typed(const Problem& p) {
   a.offset = p.offset;
   a.drop_t = p.drop_t;
   a.keep_gain = (float)(65536.0 / (65536.0 - (double)p.drop_t));
-  const int64_t grid = p.B * p.H * a.nqt;
+  a.part = p.part;
+  a.part_ml = p.part ? p.part + p.B * p.H * p.Nq * p.splits * D : nullptr;
+  a.S = (int)p.splits;
+  a.kpt = (int)p.split_tiles;
+  const int64_t grid = p.B * p.H * a.nqt * (MODE == kModeSplitKv ? p.splits : 1);
   hipLaunchKernelGGL((prefill_f32_kernel<D, TPQ, CAUSAL, MODE, KSF, NT, BN>), dim3((unsigned)grid), dim3(NT * KSF), 0,
                      p.stream, a);
   return hipGetLastError();
@@ -344,6 +374,57 @@ hipError_t launch_d(const Problem& p) {
 }
 
 }  // namespace
+
+#ifndef F32_SPLITKV
+#define F32_SPLITKV 1
+#endif
+
+bool plan_prefill_f32_splitkv(const Problem& p, SplitKvPlan* plan) {
+  // Batched FP32 problems of fewer than 512 default workgroups (the ones
+  // that would take the wide split) over at least 32 key tiles of 32 keys:
+  // the default kernel with each query tile's keys split over about four
+  // two-wave workgroups per CU, 16 key tiles a split at least (against the
+  // wide split: B1 H32 Nq512 Nk8192 D128 causal 7203 -> 1949 us, B1 H1
+  // Nq512 Nk65536 D64 causal 1896 -> 313 us, B1 H8 N2048 D64 592 -> 303
+  // us, B1 H2 N4096 D128 causal 970 -> 499 us).
+  if (!F32_SPLITKV || p.cu_q) return false;
+  const int64_t qpb = kThreads / (p.D > 64 ? 2 : 1);
+  const int64_t wq = p.B * p.H * ((p.Nq + qpb - 1) / qpb);
+  const int64_t kt = (p.Nk + kBNF - 1) / kBNF;
+  if (wq >= 512 || kt < 32) return false;
+  int64_t S = (1024 + wq - 1) / wq;
+  if (S > kt / 16) S = kt / 16;
+  // At least two workgroups per CU, else the wide split keeps more lanes
+  // busy (B1 H4 N1024 D64 causal: 2 splits x 32 workgroups 273 us, wide
+  // split 61 us).
+  if (S < 2 || wq * S < 512) return false;
+  const int64_t kpt = (kt + S - 1) / S;
+  S = (kt + kpt - 1) / kpt;
+  plan->splits = S;
+  plan->split_tiles = kpt;
+  plan->scratch_bytes =
+      (size_t)(p.B * p.H * p.Nq) * (size_t)S * (size_t)(p.D + 2) * sizeof(float);
+  return true;
+}
+
+hipError_t launch_prefill_f32_partials(const Problem& p) {
+  switch (p.D) {
+    case 16:
+      return p.causal ? launch_typed<16, kTpqDefault<16>, true, kModeSplitKv, 1, kThreads, kBNF>(p)
+                      : launch_typed<16, kTpqDefault<16>, false, kModeSplitKv, 1, kThreads, kBNF>(p);
+    case 32:
+      return p.causal ? launch_typed<32, kTpqDefault<32>, true, kModeSplitKv, 1, kThreads, kBNF>(p)
+                      : launch_typed<32, kTpqDefault<32>, false, kModeSplitKv, 1, kThreads, kBNF>(p);
+    case 64:
+      return p.causal ? launch_typed<64, kTpqDefault<64>, true, kModeSplitKv, 1, kThreads, kBNF>(p)
+                      : launch_typed<64, kTpqDefault<64>, false, kModeSplitKv, 1, kThreads, kBNF>(p);
+    case 128:
+      return p.causal
+                 ? launch_typed<128, kTpqDefault<128>, true, kModeSplitKv, 1, kThreads, kBNF>(p)
+                 : launch_typed<128, kTpqDefault<128>, false, kModeSplitKv, 1, kThreads, kBNF>(p);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_prefill_f32(const Problem& p) {
   switch (p.D) {

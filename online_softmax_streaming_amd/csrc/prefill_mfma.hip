@@ -970,12 +970,16 @@ __global__ __launch_bounds__(kCombineThreads) void splitkv_combine_kernel(
     M = mg;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  T o[4];
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4*>(out + orow * D + 4 * lr) = acc * inv;
+  } else {
+    T o[4];
   #pragma unroll
-  for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(acc[j] * inv);
-  u32x2 bits;
-  __builtin_memcpy(&bits, o, sizeof(bits));
-  *reinterpret_cast<u32x2*>(out + orow * D + 4 * lr) = bits;
+    for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(acc[j] * inv);
+    u32x2 bits;
+    __builtin_memcpy(&bits, o, sizeof(bits));
+    *reinterpret_cast<u32x2*>(out + orow * D + 4 * lr) = bits;
+  }
   if (lr == 0) {
     if (m_out) m_out[row] = M * kLn2;
     if (l_out) l_out[row] = L;
@@ -985,7 +989,9 @@ __global__ __launch_bounds__(kCombineThreads) void splitkv_combine_kernel(
 template <typename T, int D>
 hipError_t launch_splitkv_d(const Problem& p) {
   hipError_t e;
-  if (p.cu_q)
+  if constexpr (sizeof(T) == 4)
+    e = launch_prefill_f32_partials(p);  // prefill_f32.hip
+  else if (p.cu_q)
     e = p.causal ? launch_typed<T, D, kWaves, true, kModeVarlenSplitKv>(p)
                  : launch_typed<T, D, kWaves, false, kModeVarlenSplitKv>(p);
   else
@@ -1030,6 +1036,7 @@ hipError_t launch_splitkv_t(const Problem& p) {
 }  // namespace
 
 bool plan_prefill_splitkv(const Problem& p, SplitKvPlan* plan) {
+  if (p.dtype == DType::F32) return plan_prefill_f32_splitkv(p, plan);  // prefill_f32.hip
   // Query tiles of the eight-wave kernel (no causal pairing here) and key
   // tiles: few query tiles over many keys cannot fill the GPU by rows, so
   // their keys are split over workgroups, for about one workgroup per CU.
@@ -1093,7 +1100,7 @@ bool plan_prefill_splitkv(const Problem& p, SplitKvPlan* plan) {
 hipError_t launch_prefill_splitkv(const Problem& p) {
   if (p.dtype == DType::BF16) return launch_splitkv_t<__bf16>(p);
   if (p.dtype == DType::F16) return launch_splitkv_t<_Float16>(p);
-  return hipErrorInvalidValue;
+  return launch_splitkv_t<float>(p);
 }
 
 hipError_t launch_prefill_mfma(const Problem& p) {

@@ -489,3 +489,22 @@ def test_split_kv_route(b, h, nq, nk, d, causal, dtype):
     err = _compare_full(q, k, v, causal, scale, out, TOL[dtype], m, l)
     _record(f"split-kv B={b} H={h} Nq={nq} Nk={nk} D={d} causal={causal} {dtype}", err,
             TOL[dtype])
+
+
+@pytest.mark.parametrize("b,h,nq,nk,d,causal", [
+    (1, 8, 512, 8192, 64, True), (1, 2, 4096, 4096, 128, True),
+    (1, 4, 1000, 9000, 32, False), (1, 2, 700, 33000, 16, True)])
+def test_split_kv_route_f32(b, h, nq, nk, d, causal):
+    # FP32 problems too small for the default kernel to fill the GPU, over
+    # long keys: each query tile's keys split over workgroups of the default
+    # kernel (8 to 64 splits; ragged tiles) and combined.  Unramped keys keep
+    # the logits where FP32 scores carry the 1e-5 bound.
+    _say(f"split-kv f32 B={b} H={h} Nq={nq} Nk={nk} D={d} causal={causal}")
+    q, k, v = random_qkv(b, h, nq, nk, d, "f32", seed=nq + nk + d, device=DEV)
+    scale = default_scale(d)
+    out, m, l = attn_fwd_stats(q, k, v, causal=causal, scale=scale)
+    again = attn_fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(again, out), "the split-kv path is not deterministic"
+    err = _compare_full(q, k, v, causal, scale, out, TOL["f32"], m, l)
+    _record(f"split-kv f32 B={b} H={h} Nq={nq} Nk={nk} D={d} causal={causal}", err, TOL["f32"])
